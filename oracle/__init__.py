@@ -1,0 +1,215 @@
+"""numpy front-end of the plain C oracle (liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the HIP library or its binding.
+Every function here only marshals numpy arrays into the C routines declared
+in oracle.h; all arithmetic is in oracle.c.
+
+All arrays are C-contiguous numpy arrays: E4M3 codes as uint8, scales as
+float32, bf16 values as uint16 bit patterns, indices as int32, results as
+float64 (unrounded).
+"""
+import ctypes as _ct
+import os as _os
+
+import numpy as _np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _os.path.exists(_build.LIB):
+        _build.build()
+    lib = _ct.CDLL(_build.LIB)
+    P = _ct.c_void_p
+    I = _ct.c_int
+    L = _ct.c_int64
+    D = _ct.c_double
+    sig = {
+        "orc_e4m3_table": (None, [P]),
+        "orc_e4m3_encode": (_ct.c_uint8, [_ct.c_float]),
+        "orc_e4m3_encode_array": (None, [P, L, P]),
+        "orc_block_scale": (_ct.c_float, [_ct.c_float]),
+        "orc_quantize_1x128": (None, [P, I, I, I, P, P, I]),
+        "orc_quantize_128x128": (None, [P, I, I, I, P, P]),
+        "orc_bf16_to_double": (D, [_ct.c_uint16]),
+        "orc_gemm_nt_elem": (D, [P, P, I, P, P, P, I, I, I, I, I]),
+        "orc_gemm_nt": (None, [P, P, I, P, P, P, P, I, I, I]),
+        "orc_gemm_nt_at": (None, [P, P, I, P, P, P, I, I, I, P, P, L, P]),
+        "orc_block_dot": (D, [P, P]),
+        "orc_m_grouped_contiguous": (None, [P, P, P, P, P, P, P, I, I, I, I]),
+        "orc_m_grouped_contiguous_at": (None, [P, P, P, P, P, P, I, I, I, I, P, P, L, P]),
+        "orc_m_grouped_masked": (None, [P, P, P, P, P, P, P, I, I, I, I]),
+        "orc_m_grouped_masked_at": (None, [P, P, P, P, P, P, I, I, I, I, P, P, P, L, P]),
+        "orc_num_threads": (I, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _p(arr, dtype):
+    if arr is None:
+        return None
+    assert isinstance(arr, _np.ndarray), type(arr)
+    assert arr.dtype == dtype, (arr.dtype, dtype)
+    assert arr.flags["C_CONTIGUOUS"]
+    return arr.ctypes.data
+
+
+def e4m3_table():
+    out = _np.empty(256, dtype=_np.float64)
+    _load().orc_e4m3_table(out.ctypes.data)
+    return out
+
+
+def e4m3_encode(x):
+    x = _np.ascontiguousarray(x, dtype=_np.float32)
+    q = _np.empty(x.shape, dtype=_np.uint8)
+    _load().orc_e4m3_encode_array(x.ctypes.data, x.size, q.ctypes.data)
+    return q
+
+
+def block_scale(amax):
+    return _np.float32(_load().orc_block_scale(float(amax)))
+
+
+def sf_aligned(mn):
+    return (mn + 3) // 4 * 4
+
+
+def quantize_1x128(x, ld_sf=None):
+    """x[groups, rows, K] (or [rows, K]) fp32 -> (q uint8 same shape, sf[groups, K/128, ld_sf])."""
+    x = _np.ascontiguousarray(x, dtype=_np.float32)
+    squeeze = x.ndim == 2
+    x3 = x[None] if squeeze else x
+    groups, rows, K = x3.shape
+    assert K % 128 == 0
+    ld = sf_aligned(rows) if ld_sf is None else ld_sf
+    q = _np.empty(x3.shape, dtype=_np.uint8)
+    sf = _np.zeros((groups, K // 128, ld), dtype=_np.float32)
+    _load().orc_quantize_1x128(x3.ctypes.data, groups, rows, K, q.ctypes.data, sf.ctypes.data, ld)
+    if squeeze:
+        return q[0], sf[0]
+    return q, sf
+
+
+def quantize_128x128(x):
+    """x[groups, rows, K] (or [rows, K]) -> (q, sf[groups, ceil(rows/128), K/128])."""
+    x = _np.ascontiguousarray(x, dtype=_np.float32)
+    squeeze = x.ndim == 2
+    x3 = x[None] if squeeze else x
+    groups, rows, K = x3.shape
+    assert K % 128 == 0
+    q = _np.empty(x3.shape, dtype=_np.uint8)
+    sf = _np.empty((groups, (rows + 127) // 128, K // 128), dtype=_np.float32)
+    _load().orc_quantize_128x128(x3.ctypes.data, groups, rows, K, q.ctypes.data, sf.ctypes.data)
+    if squeeze:
+        return q[0], sf[0]
+    return q, sf
+
+
+def bf16_to_double(h):
+    return _load().orc_bf16_to_double(int(h))
+
+
+def block_dot(arow, brow):
+    return _load().orc_block_dot(_p(arow, _np.uint8), _p(brow, _np.uint8))
+
+
+def gemm_nt(a, sfa, b, sfb, c=None):
+    """Dense D = C + A.B^T with block scales. a[M,K], sfa[K/128, ld], b[N,K], sfb[ceil(N/128), K/128]."""
+    M, K = a.shape
+    N = b.shape[0]
+    d = _np.full((M, N), _np.nan, dtype=_np.float64)
+    _load().orc_gemm_nt(_p(a, _np.uint8), _p(sfa, _np.float32), sfa.shape[-1],
+                        _p(b, _np.uint8), _p(sfb, _np.float32), _p(c, _np.uint16),
+                        d.ctypes.data, M, N, K)
+    return d
+
+
+def gemm_nt_elem(a, sfa, b, sfb, c, m, n):
+    M, K = a.shape
+    N = b.shape[0]
+    return _load().orc_gemm_nt_elem(_p(a, _np.uint8), _p(sfa, _np.float32), sfa.shape[-1],
+                                    _p(b, _np.uint8), _p(sfb, _np.float32), _p(c, _np.uint16),
+                                    M, N, K, int(m), int(n))
+
+
+def gemm_nt_at(a, sfa, b, sfb, c, ms, ns):
+    M, K = a.shape
+    N = b.shape[0]
+    ms = _np.ascontiguousarray(ms, dtype=_np.int32)
+    ns = _np.ascontiguousarray(ns, dtype=_np.int32)
+    out = _np.empty(ms.size, dtype=_np.float64)
+    _load().orc_gemm_nt_at(_p(a, _np.uint8), _p(sfa, _np.float32), sfa.shape[-1],
+                           _p(b, _np.uint8), _p(sfb, _np.float32), _p(c, _np.uint16),
+                           M, N, K, ms.ctypes.data, ns.ctypes.data, ms.size, out.ctypes.data)
+    return out
+
+
+def m_grouped_contiguous(a, sfa, b, sfb, c, m_indices, d=None):
+    """a[M_total,K], sfa[K/128, M_total], b[G,N,K], sfb[G, ceil(N/128), K/128], m_indices[M_total]."""
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    if d is None:
+        d = _np.full((M_total, N), _np.nan, dtype=_np.float64)
+    assert sfa.shape[-1] == M_total
+    _load().orc_m_grouped_contiguous(_p(a, _np.uint8), _p(sfa, _np.float32), _p(b, _np.uint8),
+                                     _p(sfb, _np.float32), _p(c, _np.uint16),
+                                     _p(m_indices, _np.int32), _p(d, _np.float64),
+                                     M_total, N, K, G)
+    return d
+
+
+def m_grouped_contiguous_at(a, sfa, b, sfb, c, m_indices, ms, ns):
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    ms = _np.ascontiguousarray(ms, dtype=_np.int32)
+    ns = _np.ascontiguousarray(ns, dtype=_np.int32)
+    out = _np.empty(ms.size, dtype=_np.float64)
+    _load().orc_m_grouped_contiguous_at(_p(a, _np.uint8), _p(sfa, _np.float32), _p(b, _np.uint8),
+                                        _p(sfb, _np.float32), _p(c, _np.uint16),
+                                        _p(m_indices, _np.int32), M_total, N, K, G,
+                                        ms.ctypes.data, ns.ctypes.data, ms.size, out.ctypes.data)
+    return out
+
+
+def m_grouped_masked(a, sfa, b, sfb, c, masked_m, d=None):
+    """a[G,M_cap,K], sfa[G, K/128, round_up(M_cap,4)], b[G,N,K], sfb[G, ceil(N/128), K/128], masked_m[G]."""
+    G, M_cap, K = a.shape
+    N = b.shape[1]
+    if d is None:
+        d = _np.full((G, M_cap, N), _np.nan, dtype=_np.float64)
+    assert sfa.shape[-1] == sf_aligned(M_cap)
+    _load().orc_m_grouped_masked(_p(a, _np.uint8), _p(sfa, _np.float32), _p(b, _np.uint8),
+                                 _p(sfb, _np.float32), _p(c, _np.uint16),
+                                 _p(masked_m, _np.int32), _p(d, _np.float64), G, M_cap, N, K)
+    return d
+
+
+def m_grouped_masked_at(a, sfa, b, sfb, c, masked_m, gs, ms, ns):
+    G, M_cap, K = a.shape
+    N = b.shape[1]
+    gs = _np.ascontiguousarray(gs, dtype=_np.int32)
+    ms = _np.ascontiguousarray(ms, dtype=_np.int32)
+    ns = _np.ascontiguousarray(ns, dtype=_np.int32)
+    out = _np.empty(ms.size, dtype=_np.float64)
+    _load().orc_m_grouped_masked_at(_p(a, _np.uint8), _p(sfa, _np.float32), _p(b, _np.uint8),
+                                    _p(sfb, _np.float32), _p(c, _np.uint16),
+                                    _p(masked_m, _np.int32), G, M_cap, N, K,
+                                    gs.ctypes.data, ms.ctypes.data, ns.ctypes.data, ms.size,
+                                    out.ctypes.data)
+    return out
+
+
+def num_threads():
+    return _load().orc_num_threads()

@@ -1,0 +1,347 @@
+/*
+ * oracle.c -- plain CPU reference (TEST INFRASTRUCTURE ONLY; see oracle.h).
+ *
+ * Written for obviousness, not speed: table lookups, fp64 sums in the
+ * natural order, one fp64 rounding per 128-wide K block when the scaled
+ * block partial is added to the accumulator.  OpenMP only splits
+ * independent output elements (or blocks) across threads; it never changes
+ * an element's order of operations.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------------- */
+/* E4M3FN codec.  The pages name the format only as E4M3 (4-bit exponent,  */
+/* 3-bit mantissa) in the FP8 GEMM interface; the variant with no          */
+/* infinities and NaN at S.1111.111 ("fn", maximum 448) is the one the      */
+/* workload names.                                                          */
+/* ---------------------------------------------------------------------- */
+
+static double e4m3_value_from_bits(unsigned code)
+{
+    const unsigned s = (code >> 7) & 1u;
+    const unsigned e = (code >> 3) & 15u;
+    const unsigned m = code & 7u;
+    double v;
+    if (e == 15u && m == 7u)
+        return NAN;                         /* the only NaN encodings */
+    if (e == 0u)
+        v = ldexp((double)m / 8.0, 1 - 7);  /* subnormal: 2^-6 * m/8 */
+    else
+        v = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -v : v;
+}
+
+static double T[256];
+static int T_ready = 0;
+
+static void table_init(void)
+{
+    if (T_ready)
+        return;
+    for (unsigned c = 0; c < 256u; ++c)
+        T[c] = e4m3_value_from_bits(c);
+    T_ready = 1;
+}
+
+void orc_e4m3_table(double out[256])
+{
+    table_init();
+    for (int c = 0; c < 256; ++c)
+        out[c] = T[c];
+}
+
+uint8_t orc_e4m3_encode(float x)
+{
+    table_init();
+    if (x != x)
+        return 0x7F;
+    const uint8_t s = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs((double)x);
+    if (a >= 448.0)
+        return (uint8_t)(s | 0x7E);         /* saturate at the largest finite */
+    /* Positive finite codes 0x00..0x7E are strictly increasing in value.
+     * Find lo, hi = lo + 1 with T[lo] <= a < T[hi]. */
+    int lo = 0, hi = 0x7E;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (T[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const double dlo = a - T[lo];           /* exact: same binade as a */
+    const double dhi = T[hi] - a;
+    int pick;
+    if (dlo < dhi)
+        pick = lo;
+    else if (dhi < dlo)
+        pick = hi;
+    else
+        pick = (lo & 1) ? hi : lo;          /* tie: even mantissa */
+    return (uint8_t)(s | pick);
+}
+
+void orc_e4m3_encode_array(const float *x, int64_t n, uint8_t *q)
+{
+    table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = orc_e4m3_encode(x[i]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Quantisers.  Scale per block = amax/448 (the largest E4M3 magnitude),    */
+/* with amax floored at 1e-4 so that an all-zero block has a finite scale.  */
+/* Each element is divided by its block scale in fp32 and cast with         */
+/* round-to-nearest-even.                                                   */
+/* ---------------------------------------------------------------------- */
+
+float orc_block_scale(float amax)
+{
+    const float floor_amax = 1e-4f;
+    const float a = amax > floor_amax ? amax : floor_amax;
+    return a / 448.0f;
+}
+
+void orc_quantize_1x128(const float *x, int groups, int rows, int K,
+                        uint8_t *q, float *sf, int ld_sf)
+{
+    table_init();
+    const int nkb = K / 128;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int g = 0; g < groups; ++g)
+        for (int r = 0; r < rows; ++r)
+            for (int kb = 0; kb < nkb; ++kb) {
+                const size_t base = ((size_t)g * rows + r) * (size_t)K + (size_t)kb * 128;
+                float amax = 0.0f;
+                for (int k = 0; k < 128; ++k) {
+                    const float v = fabsf(x[base + k]);
+                    if (v > amax)
+                        amax = v;
+                }
+                const float s = orc_block_scale(amax);
+                for (int k = 0; k < 128; ++k)
+                    q[base + k] = orc_e4m3_encode(x[base + k] / s);
+                sf[((size_t)g * nkb + kb) * (size_t)ld_sf + r] = s;
+            }
+}
+
+void orc_quantize_128x128(const float *x, int groups, int rows, int K,
+                          uint8_t *q, float *sf)
+{
+    table_init();
+    const int nkb = K / 128;
+    const int nrb = (rows + 127) / 128;
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int g = 0; g < groups; ++g)
+        for (int rb = 0; rb < nrb; ++rb)
+            for (int kb = 0; kb < nkb; ++kb) {
+                const int r0 = rb * 128;
+                const int r1 = r0 + 128 < rows ? r0 + 128 : rows;
+                float amax = 0.0f;
+                for (int r = r0; r < r1; ++r)
+                    for (int k = 0; k < 128; ++k) {
+                        const float v = fabsf(x[((size_t)g * rows + r) * (size_t)K + (size_t)kb * 128 + k]);
+                        if (v > amax)
+                            amax = v;
+                    }
+                const float s = orc_block_scale(amax);
+                for (int r = r0; r < r1; ++r)
+                    for (int k = 0; k < 128; ++k) {
+                        const size_t i = ((size_t)g * rows + r) * (size_t)K + (size_t)kb * 128 + k;
+                        q[i] = orc_e4m3_encode(x[i] / s);
+                    }
+                sf[((size_t)g * nrb + rb) * (size_t)nkb + kb] = s;
+            }
+}
+
+/* ---------------------------------------------------------------------- */
+/* GEMM.                                                                    */
+/* ---------------------------------------------------------------------- */
+
+double orc_bf16_to_double(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double orc_block_dot(const uint8_t *arow, const uint8_t *brow)
+{
+    table_init();
+    double p = 0.0;
+    for (int k = 0; k < 128; ++k)
+        p += T[arow[k]] * T[brow[k]];
+    return p;
+}
+
+double orc_gemm_nt_elem(const uint8_t *a, const float *sfa, int ld_sfa,
+                        const uint8_t *b, const float *sfb, const uint16_t *c,
+                        int M, int N, int K, int m, int n)
+{
+    (void)M;
+    table_init();
+    const int nkb = K / 128;
+    const uint8_t *arow = a + (size_t)m * K;
+    const uint8_t *brow = b + (size_t)n * K;
+    const int nb = n / 128;
+    double acc = 0.0;
+    for (int kb = 0; kb < nkb; ++kb) {
+        /* block partial: exact in fp64 */
+        double p = 0.0;
+        for (int k = kb * 128; k < kb * 128 + 128; ++k)
+            p += T[arow[k]] * T[brow[k]];
+        /* product of two fp32 scales: exact in fp64 */
+        const double s = (double)sfa[(size_t)kb * ld_sfa + m] * (double)sfb[(size_t)nb * nkb + kb];
+        acc += p * s;
+    }
+    if (c)
+        acc += orc_bf16_to_double(c[(size_t)m * N + n]);
+    return acc;
+}
+
+void orc_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa,
+                 const uint8_t *b, const float *sfb, const uint16_t *c,
+                 double *d, int M, int N, int K)
+{
+    table_init();
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n)
+            d[(size_t)m * N + n] = orc_gemm_nt_elem(a, sfa, ld_sfa, b, sfb, c, M, N, K, m, n);
+}
+
+void orc_gemm_nt_at(const uint8_t *a, const float *sfa, int ld_sfa,
+                    const uint8_t *b, const float *sfb, const uint16_t *c,
+                    int M, int N, int K, const int32_t *ms, const int32_t *ns,
+                    int64_t count, double *out)
+{
+    table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = orc_gemm_nt_elem(a, sfa, ld_sfa, b, sfb, c, M, N, K, ms[i], ns[i]);
+}
+
+/* Contiguous layout: rows of all experts concatenated along M; the expert of
+ * row r is m_indices[r], negative on padding rows. */
+static double contiguous_elem(const uint8_t *a, const float *sfa,
+                              const uint8_t *b, const float *sfb,
+                              const uint16_t *c, int g,
+                              int M_total, int N, int K, int r, int n)
+{
+    const size_t nbk = (size_t)((N + 127) / 128) * (size_t)(K / 128);
+    return orc_gemm_nt_elem(a, sfa, M_total,
+                            b + (size_t)g * N * K, sfb + (size_t)g * nbk,
+                            c, M_total, N, K, r, n);
+}
+
+void orc_m_grouped_contiguous(const uint8_t *a, const float *sfa,
+                              const uint8_t *b, const float *sfb,
+                              const uint16_t *c, const int32_t *m_indices,
+                              double *d, int M_total, int N, int K, int G)
+{
+    (void)G;
+    table_init();
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int r = 0; r < M_total; ++r)
+        for (int n = 0; n < N; ++n) {
+            const int g = m_indices[r];
+            if (g < 0)
+                continue;                   /* padding row: untouched */
+            d[(size_t)r * N + n] = contiguous_elem(a, sfa, b, sfb, c, g, M_total, N, K, r, n);
+        }
+}
+
+void orc_m_grouped_contiguous_at(const uint8_t *a, const float *sfa,
+                                 const uint8_t *b, const float *sfb,
+                                 const uint16_t *c, const int32_t *m_indices,
+                                 int M_total, int N, int K, int G,
+                                 const int32_t *ms, const int32_t *ns,
+                                 int64_t count, double *out)
+{
+    (void)G;
+    table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        const int g = m_indices[ms[i]];
+        out[i] = g < 0 ? NAN : contiguous_elem(a, sfa, b, sfb, c, g, M_total, N, K, ms[i], ns[i]);
+    }
+}
+
+/* Masked layout: group g owns M_cap rows, of which the first masked_m[g]
+ * (clamped to [0, M_cap]) are valid. */
+static int masked_rows(const int32_t *masked_m, int g, int M_cap)
+{
+    int v = masked_m[g];
+    if (v < 0)
+        v = 0;
+    if (v > M_cap)
+        v = M_cap;
+    return v;
+}
+
+static double masked_elem(const uint8_t *a, const float *sfa,
+                          const uint8_t *b, const float *sfb,
+                          const uint16_t *c, int G, int M_cap, int N, int K,
+                          int g, int r, int n)
+{
+    (void)G;
+    const int ld = (M_cap + 3) / 4 * 4;
+    const size_t nkb = (size_t)(K / 128);
+    const size_t nbk = (size_t)((N + 127) / 128) * nkb;
+    return orc_gemm_nt_elem(a + (size_t)g * M_cap * K, sfa + (size_t)g * nkb * ld, ld,
+                            b + (size_t)g * N * K, sfb + (size_t)g * nbk,
+                            c ? c + (size_t)g * M_cap * N : NULL,
+                            M_cap, N, K, r, n);
+}
+
+void orc_m_grouped_masked(const uint8_t *a, const float *sfa,
+                          const uint8_t *b, const float *sfb,
+                          const uint16_t *c, const int32_t *masked_m,
+                          double *d, int G, int M_cap, int N, int K)
+{
+    table_init();
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int g = 0; g < G; ++g)
+        for (int r = 0; r < M_cap; ++r)
+            for (int n = 0; n < N; ++n) {
+                if (r >= masked_rows(masked_m, g, M_cap))
+                    continue;               /* masked row: untouched */
+                d[((size_t)g * M_cap + r) * N + n] =
+                    masked_elem(a, sfa, b, sfb, c, G, M_cap, N, K, g, r, n);
+            }
+}
+
+void orc_m_grouped_masked_at(const uint8_t *a, const float *sfa,
+                             const uint8_t *b, const float *sfb,
+                             const uint16_t *c, const int32_t *masked_m,
+                             int G, int M_cap, int N, int K,
+                             const int32_t *gs, const int32_t *ms,
+                             const int32_t *ns, int64_t count, double *out)
+{
+    table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = ms[i] >= masked_rows(masked_m, gs[i], M_cap)
+                     ? NAN
+                     : masked_elem(a, sfa, b, sfb, c, G, M_cap, N, K, gs[i], ms[i], ns[i]);
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

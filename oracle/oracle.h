@@ -1,0 +1,132 @@
+/*
+ * oracle.h -- plain CPU reference for the FP8 block-scaled NT GEMM and its
+ * M-grouped variants.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant generator with the HIP library, and the HIP
+ * library never calls it.
+ *
+ * Sources (the web pages about DeepGEMM; cited by page title and section):
+ *  - "DeepGEMM" README summary on GeekNews (ja.news.hada.io, topic 19459),
+ *    section "GEMM interface and layout constraints": D = C + A @ B.T in the
+ *    NT layout, E4M3 inputs, FP32 scaling factors, LHS scales transposed.
+ *  - same page, section "Dense and Grouped GEMM": M-grouped contiguous layout
+ *    (expert segments aligned to the M block) and masked layout (only the
+ *    valid rows of each group are computed).
+ *  - "DeepSeek open-sources DeepGEMM" news (picoinsstore.com), paragraph on
+ *    the two-level accumulation: the low-precision tensor-core partial is
+ *    promoted into a higher-precision accumulator.
+ *  The block granularity (1x128 for A, 128x128 for B), the scale formula
+ *  sf = amax/448 and the round-to-nearest-even cast are the workload
+ *  definition; the pages call the scaling only "fine-grained".
+ *
+ * Precision: everything that is not an E4M3 code, an fp32 scale or a bf16
+ * bit pattern is fp64.  A 128-term block sum of E4M3 products is exact in
+ * fp64 (every E4M3 value is a multiple of 2^-9 below 2^9, so a product is a
+ * multiple of 2^-18 below 2^18 and 128 of them stay below 2^43 units).
+ *
+ * Parity pins: every function here is pinned by tests that do not re-type
+ * its formula (exhaustive codec checks against torch's float8_e4m3fn,
+ * closed-form scale cases, numpy matmul of the de-scaled operands, integer
+ * evaluation of block sums, identity/one-hot products, grouped == per-group
+ * dense).  None is "parity unpinned".
+ */
+#ifndef DG_ORACLE_H
+#define DG_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* E4M3FN (OCP 8-bit float: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, 0x7F/0xFF are NaN) decoded to fp64 for all 256 codes. */
+void orc_e4m3_table(double out[256]);
+
+/* Nearest E4M3FN value to x, ties to the even code, saturating to +-448.
+ * NaN -> 0x7F.  The sign of zero is kept. */
+uint8_t orc_e4m3_encode(float x);
+void orc_e4m3_encode_array(const float *x, int64_t n, uint8_t *q);
+
+/* Block scale: max(amax, 1e-4f) / 448.0f as one fp32 division. */
+float orc_block_scale(float amax);
+
+/* 1x128 quantiser: x[groups][rows][K] fp32 -> q[groups][rows][K] E4M3 and
+ * sf[groups][K/128][ld_sf] (one scale per row and 128-wide K block, stored
+ * K-block-major, i.e. transposed).  Entries of sf with row index >= rows are
+ * not written. */
+void orc_quantize_1x128(const float *x, int groups, int rows, int K,
+                        uint8_t *q, float *sf, int ld_sf);
+
+/* 128x128 quantiser: x[groups][rows][K] -> q, sf[groups][ceil(rows/128)][K/128].
+ * The last row block of a group may be partial; blocks never straddle groups. */
+void orc_quantize_128x128(const float *x, int groups, int rows, int K,
+                          uint8_t *q, float *sf);
+
+/* bf16 bit pattern -> fp64 (exact). */
+double orc_bf16_to_double(uint16_t h);
+
+/* One output element of D = C + A.B^T with per-block scales:
+ *   D[m,n] = C[m,n] + sum_kb sfa[kb][m] * sfb[n/128][kb] * sum_{k in kb} A[m,k] B[n,k]
+ * a[M][K], sfa[K/128][ld_sfa], b[N][K], sfb[ceil(N/128)][K/128], c[M][N] or NULL. */
+double orc_gemm_nt_elem(const uint8_t *a, const float *sfa, int ld_sfa,
+                        const uint8_t *b, const float *sfb, const uint16_t *c,
+                        int M, int N, int K, int m, int n);
+
+/* Full dense result d[M][N] (fp64, unrounded). */
+void orc_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa,
+                 const uint8_t *b, const float *sfb, const uint16_t *c,
+                 double *d, int M, int N, int K);
+
+/* Selected elements: out[i] = D[ms[i], ns[i]]. */
+void orc_gemm_nt_at(const uint8_t *a, const float *sfa, int ld_sfa,
+                    const uint8_t *b, const float *sfb, const uint16_t *c,
+                    int M, int N, int K, const int32_t *ms, const int32_t *ns,
+                    int64_t count, double *out);
+
+/* The 128-element block sum alone, p = sum_{k in kb} A[m,k] B[n,k] (exact). */
+double orc_block_dot(const uint8_t *arow, const uint8_t *brow);
+
+/* M-grouped contiguous: a[M_total][K], sfa[K/128][M_total], b[G][N][K],
+ * sfb[G][ceil(N/128)][K/128], c[M_total][N] or NULL, m_indices[M_total].
+ * Row r with g = m_indices[r] >= 0 gets the dense result against B[g];
+ * rows with m_indices[r] < 0 are left untouched in d[M_total][N]. */
+void orc_m_grouped_contiguous(const uint8_t *a, const float *sfa,
+                              const uint8_t *b, const float *sfb,
+                              const uint16_t *c, const int32_t *m_indices,
+                              double *d, int M_total, int N, int K, int G);
+
+/* Same, only for rows rows[0..count): used to sample large problems. */
+void orc_m_grouped_contiguous_at(const uint8_t *a, const float *sfa,
+                                 const uint8_t *b, const float *sfb,
+                                 const uint16_t *c, const int32_t *m_indices,
+                                 int M_total, int N, int K, int G,
+                                 const int32_t *ms, const int32_t *ns,
+                                 int64_t count, double *out);
+
+/* M-grouped masked: a[G][M_cap][K], sfa[G][K/128][round_up(M_cap,4)],
+ * b[G][N][K], sfb[G][ceil(N/128)][K/128], c[G][M_cap][N] or NULL,
+ * masked_m[G].  Rows r < clamp(masked_m[g], 0, M_cap) of group g get the dense
+ * result of A[g] against B[g]; every other row of d[G][M_cap][N] is untouched. */
+void orc_m_grouped_masked(const uint8_t *a, const float *sfa,
+                          const uint8_t *b, const float *sfb,
+                          const uint16_t *c, const int32_t *masked_m,
+                          double *d, int G, int M_cap, int N, int K);
+
+/* Same for selected (g, m, n) triples; out[i] is NaN when the row is masked. */
+void orc_m_grouped_masked_at(const uint8_t *a, const float *sfa,
+                             const uint8_t *b, const float *sfb,
+                             const uint16_t *c, const int32_t *masked_m,
+                             int G, int M_cap, int N, int K,
+                             const int32_t *gs, const int32_t *ms,
+                             const int32_t *ns, int64_t count, double *out);
+
+/* Number of OpenMP threads the oracle uses (for reporting). */
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

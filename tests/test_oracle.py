@@ -1,0 +1,416 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test names what it pins and where that fact comes from:
+  * the E4M3FN codec against torch's float8_e4m3fn (a library routine) and
+    the closed-form code table in tests/golden/e4m3fn_codes.txt;
+  * the encoder's round-to-nearest-even against torch's cast over every fp32
+    bit pattern in the E4M3 range, and against the midpoint definition;
+  * the quantisers against inputs whose result is known in closed form
+    (blocks of exactly representable values with a power-of-two amax);
+  * the GEMM against numpy matmul of the de-scaled operands, against integer
+    evaluation of a block sum, and against identity/one-hot products;
+  * the grouped variants against per-group dense results.
+A mistake such as a transposed scale index, a dropped C term or a wrong
+tie rule fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_grouped_gemm_scaled_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def torch_decode(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def torch_encode(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+# ---------------------------------------------------------------- codec
+
+
+def test_table_equals_torch_float8_e4m3fn():
+    table = oracle.e4m3_table()
+    ref = torch_decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(table), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(table[ok], ref[ok])
+    # the sign of zero is part of the format
+    assert np.signbit(table[0x80]) and not np.signbit(table[0x00])
+    assert np.isnan(table[0x7F]) and np.isnan(table[0xFF])
+    assert int(np.isnan(table).sum()) == 2
+
+
+def test_table_matches_ocp_golden_values():
+    table = oracle.e4m3_table()
+    n = 0
+    with open(os.path.join(GOLDEN, "e4m3fn_codes.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            code_s, val_s = line.split()
+            code = int(code_s, 16)
+            if val_s == "nan":
+                assert np.isnan(table[code])
+            else:
+                v = float(val_s)
+                assert table[code] == v, (hex(code), table[code], v)
+                assert np.signbit(table[code]) == val_s.startswith("-")
+            n += 1
+    assert n >= 20
+
+
+def test_table_monotone_and_symmetric():
+    table = oracle.e4m3_table()
+    pos = table[0x00:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(table[0x80:0xFF], -pos)
+
+
+def test_encode_decode_roundtrip_all_finite_codes():
+    table = oracle.e4m3_table()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    back = oracle.e4m3_encode(table[codes].astype(np.float32))
+    assert np.array_equal(back, codes)
+
+
+def _binade_patterns(lo_exp: int, hi_exp: int) -> np.ndarray:
+    """All fp32 bit patterns with biased exponent in [lo_exp, hi_exp]."""
+    lo = np.uint32(lo_exp << 23)
+    hi = np.uint32((hi_exp + 1) << 23)
+    return np.arange(lo, hi, dtype=np.uint32)
+
+
+def test_encode_equals_torch_on_every_fp32_in_range():
+    """Every fp32 with 2^-12 <= |x| < 448 (both signs): the oracle encoder and
+    torch's round-to-nearest-even cast agree bit for bit.  Above 448 torch does
+    not saturate, so that range is pinned separately."""
+    n_checked = 0
+    for e in range(127 - 12, 127 + 9):          # binades [2^-12, 2^9)
+        bits = _binade_patterns(e, e)
+        x = bits.view(np.float32)
+        x = x[x < 448.0]
+        for sign in (1.0, -1.0):
+            xs = (x * np.float32(sign)).astype(np.float32)
+            got = oracle.e4m3_encode(xs)
+            ref = torch_encode(xs)
+            bad = np.nonzero(got != ref)[0]
+            assert bad.size == 0, (e, xs[bad[:4]], got[bad[:4]], ref[bad[:4]])
+            n_checked += xs.size
+    assert n_checked > 300_000_000
+
+
+def test_encode_saturates_and_tiny_values():
+    big = np.array([448.0, 448.5, 463.99, 464.0, 479.0, 480.0, 1e6, 3.4e38, np.inf], dtype=np.float32)
+    assert np.all(oracle.e4m3_encode(big) == 0x7E)
+    assert np.all(oracle.e4m3_encode(-big) == 0xFE)
+    # |x| <= 2^-10 (half the smallest subnormal) rounds to zero, keeping the sign
+    tiny = np.array([0.0, 2.0 ** -149, 1e-30, 2.0 ** -11, 2.0 ** -10], dtype=np.float32)
+    assert np.all(oracle.e4m3_encode(tiny) == 0x00)
+    assert np.all(oracle.e4m3_encode(-tiny) == 0x80)
+    just_above = np.nextafter(np.float32(2.0 ** -10), np.float32(1.0))
+    assert oracle.e4m3_encode(np.array([just_above]))[0] == 0x01
+    assert oracle.e4m3_encode(np.array([np.nan], dtype=np.float32))[0] == 0x7F
+
+
+def test_encode_midpoints_round_to_even():
+    """Round to nearest, ties to even, by definition: the midpoint of two
+    neighbouring codes goes to the one with an even mantissa; one fp32 ulp
+    either side goes to the nearer one."""
+    table = oracle.e4m3_table()
+    for c in range(0x00, 0x7E):
+        lo, hi = table[c], table[c + 1]
+        mid = np.float32((lo + hi) / 2.0)
+        assert float(mid) == (lo + hi) / 2.0          # midpoints are fp32-exact
+        even = c if c % 2 == 0 else c + 1
+        below = np.nextafter(mid, np.float32(-1.0))
+        above = np.nextafter(mid, np.float32(1e9))
+        got = oracle.e4m3_encode(np.array([mid, below, above], dtype=np.float32))
+        assert list(got) == [even, c, c + 1], (hex(c), got)
+
+
+# ---------------------------------------------------------------- quantisers
+
+
+def _representable_blocks(rows, K, seed, block_rows):
+    """x = dec(codes) * 2^j, one j per block, each block containing +-448:
+    amax = 448 * 2^j, so the scale is exactly 2^j and the codes come back."""
+    codes = synth.random_codes(seed, 0, (rows, K))
+    nrb = (rows + block_rows - 1) // block_rows
+    nkb = K // 128
+    j = synth.randint(seed, 3, nrb * nkb, -20, 20).reshape(nrb, nkb)
+    for rb in range(nrb):
+        for kb in range(nkb):
+            r0 = rb * block_rows
+            codes[r0, kb * 128 + (rb * 7 + kb * 13) % 128] = 0x7E if (rb + kb) % 2 == 0 else 0xFE
+    vals = torch_decode(codes)
+    scale = np.ldexp(1.0, np.repeat(np.repeat(j, block_rows, axis=0)[:rows], 128, axis=1))
+    x = (vals * scale).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), vals * scale)   # exact
+    return codes, j, x
+
+
+def test_quantize_1x128_exact_on_representable_blocks():
+    rows, K = 37, 384
+    codes, j, x = _representable_blocks(rows, K, seed=11, block_rows=1)
+    q, sf = oracle.quantize_1x128(x)
+    assert np.array_equal(q, codes)
+    assert sf.shape == (K // 128, 40)       # transposed, rows padded to a multiple of 4
+    assert np.array_equal(sf[:, :rows], np.ldexp(np.float32(1.0), j.T).astype(np.float32))
+
+
+def test_quantize_128x128_exact_on_representable_blocks():
+    rows, K = 300, 256                      # last row block is partial (44 rows)
+    codes, j, x = _representable_blocks(rows, K, seed=12, block_rows=128)
+    q, sf = oracle.quantize_128x128(x)
+    assert np.array_equal(q, codes)
+    assert sf.shape == (3, 2)
+    assert np.array_equal(sf, np.ldexp(np.float32(1.0), j).astype(np.float32))
+
+
+def test_quantize_zero_block_and_scale_floor():
+    x = np.zeros((4, 256), dtype=np.float32)
+    x[1, 130] = 2.0
+    q, sf = oracle.quantize_1x128(x)
+    floor_sf = np.float32(np.float32(1e-4) / np.float32(448.0))
+    assert np.all(q[0] == 0) and np.all(q[1, :128] == 0)
+    assert sf[0, 0] == floor_sf and sf[1, 0] == floor_sf
+    assert sf[1, 1] == np.float32(2.0) / np.float32(448.0)
+    assert q[1, 130] == 0x7E
+
+
+def _e4m3_half_spacing(y):
+    ay = np.abs(y)
+    e = np.floor(np.log2(np.maximum(ay, 2.0 ** -6)))
+    return np.ldexp(1.0, (e - 3).astype(int)) / 2.0
+
+
+@pytest.mark.parametrize("kind", ["1x128", "128x128"])
+def test_quantize_invariants_on_normal_data(kind):
+    x = synth.normal_f32(21, 0, (260, 512))
+    if kind == "1x128":
+        q, sf = oracle.quantize_1x128(x)
+        s_full = np.repeat(sf[:, :260].T, 128, axis=1)
+    else:
+        q, sf = oracle.quantize_128x128(x)
+        s_full = np.repeat(np.repeat(sf, 128, axis=0)[:260], 128, axis=1)
+    vals = torch_decode(q)
+    y = x.astype(np.float64) / s_full
+    # round-to-nearest within half a spacing (+ the fp32 division's rounding)
+    err = np.abs(vals - y)
+    assert np.all(err <= _e4m3_half_spacing(y) + np.abs(y) * 2.0 ** -23)
+    # the element of largest magnitude in each block maps to +-448
+    blocks = np.abs(vals).reshape(-1) if kind == "1x128" else None
+    if kind == "1x128":
+        per_block = np.abs(vals).reshape(260, 4, 128).max(axis=2)
+        assert np.all(per_block == 448.0)
+    else:
+        for rb in range(3):
+            for kb in range(4):
+                blk = np.abs(vals[rb * 128:(rb + 1) * 128, kb * 128:(kb + 1) * 128])
+                assert blk.max() == 448.0
+    del blocks
+
+
+def test_quantize_groups_do_not_share_blocks_and_ld_padding_untouched():
+    x = synth.normal_f32(22, 0, (2, 130, 256))
+    x[1] *= 100.0
+    q, sf = oracle.quantize_128x128(x)
+    for g in range(2):
+        qg, sfg = oracle.quantize_128x128(x[g])
+        assert np.array_equal(q[g], qg) and np.array_equal(sf[g], sfg)
+    q1, sf1 = oracle.quantize_1x128(x, ld_sf=136)
+    assert np.all(sf1[:, :, 130:] == 0.0)        # zero-initialised padding stays
+    for g in range(2):
+        qg, sfg = oracle.quantize_1x128(x[g])
+        assert np.array_equal(q1[g], qg) and np.array_equal(sf1[g][:, :130], sfg[:, :130])
+
+
+# ---------------------------------------------------------------- GEMM
+
+
+def _expand_scales(sfa, sfb, M, N, K):
+    SA = np.repeat(sfa[:, :M].astype(np.float64).T, 128, axis=1)          # [M, K]
+    SB = np.repeat(np.repeat(sfb.astype(np.float64), 128, axis=0)[:N], 128, axis=1)  # [N, K]
+    return SA, SB
+
+
+def _random_problem(M, N, K, seed, with_c=True):
+    a = synth.random_codes(seed, 0, (M, K))
+    b = synth.random_codes(seed, 1, (N, K))
+    ld = oracle.sf_aligned(M)
+    sfa = np.zeros((K // 128, ld), dtype=np.float32)
+    sfa[:, :M] = (synth.uniform(seed, 4, (K // 128) * M).reshape(K // 128, M) * 4 + 0.01).astype(np.float32)
+    sfb = (synth.uniform(seed, 5, ((N + 127) // 128) * (K // 128)).reshape(-1, K // 128) * 4 + 0.01).astype(np.float32)
+    c = synth.normal_bf16_bits(seed, 2, (M, N)) if with_c else None
+    return a, sfa, b, sfb, c
+
+
+@pytest.mark.parametrize("M,N,K,with_c", [(37, 200, 384, True), (5, 131, 256, False), (64, 1, 128, True)])
+def test_gemm_equals_matmul_of_descaled_operands(M, N, K, with_c):
+    """sum_kb sfa*sfb*blocksum == (dec(A)*SA) @ (dec(B)*SB)^T: scales are constant
+    inside a block, so the two agree in exact arithmetic.  numpy's float64
+    matmul is the library routine; the bound is its own rounding."""
+    a, sfa, b, sfb, c = _random_problem(M, N, K, seed=M * 1000 + N)
+    d = oracle.gemm_nt(a, sfa, b, sfb, c)
+    SA, SB = _expand_scales(sfa, sfb, M, N, K)
+    Ad = torch_decode(a) * SA
+    Bd = torch_decode(b) * SB
+    ref = Ad @ Bd.T
+    if c is not None:
+        ref = ref + synth.bf16_bits_to_f32(c).astype(np.float64)
+    mag = np.abs(Ad) @ np.abs(Bd).T + (0 if c is None else np.abs(synth.bf16_bits_to_f32(c)))
+    assert np.all(np.abs(d - ref) <= mag * 2.0 ** -48)
+
+
+def test_gemm_single_block_unit_scales_is_exact_matmul():
+    M, N, K = 19, 23, 128
+    a = synth.random_codes(31, 0, (M, K))
+    b = synth.random_codes(31, 1, (N, K))
+    sfa = np.ones((1, oracle.sf_aligned(M)), dtype=np.float32)
+    sfb = np.ones((1, 1), dtype=np.float32)
+    d = oracle.gemm_nt(a, sfa, b, sfb, None)
+    ref = torch_decode(a) @ torch_decode(b).T          # every partial sum is exact
+    assert np.array_equal(d, ref)
+
+
+def test_block_dot_is_exact_integer_sum():
+    """Block sum in units of 2^-18 from integer arithmetic on decoded values."""
+    a = synth.random_codes(41, 0, (50, 128))
+    b = synth.random_codes(41, 1, (50, 128))
+    a[0, :] = 0x7E
+    b[0, :] = 0x7E                       # largest magnitude products
+    a[1, :] = 0x01
+    b[1, :] = 0x81                       # smallest subnormal products
+    ia = (torch_decode(a) * 512).astype(np.int64)
+    ib = (torch_decode(b) * 512).astype(np.int64)
+    assert np.array_equal(ia.astype(np.float64) / 512, torch_decode(a))
+    for i in range(50):
+        exact = int(np.sum(ia[i] * ib[i]))
+        assert oracle.block_dot(a[i], b[i]) == exact / 2.0 ** 18
+
+
+def test_gemm_identity_and_power_of_two_scales_exact():
+    """B = identity (code 0x38 = 1.0 on the diagonal), power-of-two scales: every
+    D[m,n] is the single product dec(A[m,n]) * sfa[n/128][m] * sfb[n/128][n/128]."""
+    M, K = 40, 384
+    N = K
+    a = synth.random_codes(51, 0, (M, K))
+    b = np.zeros((N, K), dtype=np.uint8)
+    b[np.arange(N), np.arange(N)] = 0x38
+    ea = synth.randint(51, 4, (K // 128) * M, -8, 8).reshape(K // 128, M)
+    eb = synth.randint(51, 5, (N // 128) * (K // 128), -8, 8).reshape(N // 128, K // 128)
+    sfa = np.zeros((K // 128, oracle.sf_aligned(M)), dtype=np.float32)
+    sfa[:, :M] = np.ldexp(1.0, ea)
+    sfb = np.ldexp(np.float32(1.0), eb).astype(np.float32)
+    d = oracle.gemm_nt(a, sfa, b, sfb, None)
+    av = torch_decode(a)
+    for n in range(N):
+        kb = n // 128
+        expect = av[:, n] * sfa[kb, :M].astype(np.float64) * float(sfb[kb, kb])
+        assert np.array_equal(d[:, n], expect)
+
+
+def test_gemm_zero_a_returns_c_exactly():
+    M, N, K = 9, 140, 256
+    a = np.zeros((M, K), dtype=np.uint8)
+    _, sfa, b, sfb, c = _random_problem(M, N, K, seed=61)
+    d = oracle.gemm_nt(a, sfa, b, sfb, c)
+    assert np.array_equal(d, synth.bf16_bits_to_f32(c).astype(np.float64))
+
+
+def test_gemm_elem_at_and_full_agree():
+    M, N, K = 33, 150, 256
+    a, sfa, b, sfb, c = _random_problem(M, N, K, seed=71)
+    d = oracle.gemm_nt(a, sfa, b, sfb, c)
+    ms = synth.randint(71, 6, 100, 0, M - 1)
+    ns = synth.randint(71, 7, 100, 0, N - 1)
+    at = oracle.gemm_nt_at(a, sfa, b, sfb, c, ms, ns)
+    assert np.array_equal(at, d[ms, ns])
+    assert oracle.gemm_nt_elem(a, sfa, b, sfb, c, 5, 149) == d[5, 149]
+
+
+# ---------------------------------------------------------------- grouped
+
+
+def _contiguous_problem(counts, N, K, seed):
+    m_idx = synth.contiguous_m_indices(counts)
+    M_total = m_idx.size
+    G = len(counts)
+    a = synth.random_codes(seed, 0, (M_total, K))
+    b = synth.random_codes(seed, 1, (G, N, K))
+    sfa = (synth.uniform(seed, 4, (K // 128) * M_total).reshape(K // 128, M_total) + 0.5).astype(np.float32)
+    sfb = (synth.uniform(seed, 5, G * ((N + 127) // 128) * (K // 128)).reshape(G, -1, K // 128) + 0.5).astype(np.float32)
+    c = synth.normal_bf16_bits(seed, 2, (M_total, N))
+    return a, sfa, b, sfb, c, m_idx
+
+
+def test_contiguous_equals_per_group_dense_and_skips_padding():
+    counts = [1, 128, 130, 0, 77]
+    N, K = 136, 256
+    a, sfa, b, sfb, c, m_idx = _contiguous_problem(counts, N, K, seed=81)
+    assert m_idx.size % 128 == 0
+    d = oracle.m_grouped_contiguous(a, sfa, b, sfb, c, m_idx)
+    for g in range(len(counts)):
+        rows = np.nonzero(m_idx == g)[0]
+        assert rows.size == counts[g]
+        if rows.size == 0:
+            continue
+        dense = oracle.gemm_nt(np.ascontiguousarray(a[rows]),
+                               np.ascontiguousarray(np.pad(sfa[:, rows], ((0, 0), (0, (-rows.size) % 4)))),
+                               np.ascontiguousarray(b[g]), np.ascontiguousarray(sfb[g]),
+                               np.ascontiguousarray(c[rows]))
+        assert np.array_equal(d[rows], dense)
+    assert np.all(np.isnan(d[m_idx < 0]))
+    ms = np.arange(m_idx.size, dtype=np.int32)
+    ns = (ms * 7) % N
+    at = oracle.m_grouped_contiguous_at(a, sfa, b, sfb, c, m_idx, ms, ns)
+    assert np.array_equal(np.isnan(at), m_idx < 0)
+    ok = m_idx >= 0
+    assert np.array_equal(at[ok], d[ms[ok], ns[ok]])
+
+
+def test_masked_equals_per_group_dense_and_leaves_rows_untouched():
+    G, M_cap, N, K = 5, 130, 72, 256
+    seed = 91
+    a = synth.random_codes(seed, 0, (G, M_cap, K))
+    b = synth.random_codes(seed, 1, (G, N, K))
+    ld = oracle.sf_aligned(M_cap)
+    sfa = (synth.uniform(seed, 4, G * (K // 128) * ld).reshape(G, K // 128, ld) + 0.5).astype(np.float32)
+    sfb = (synth.uniform(seed, 5, G * 1 * (K // 128)).reshape(G, 1, K // 128) + 0.5).astype(np.float32)
+    masked_m = np.array([0, 1, 129, 130, 500], dtype=np.int32)   # 500 clamps to M_cap
+    d = oracle.m_grouped_masked(a, sfa, b, sfb, None, masked_m)
+    for g in range(G):
+        mm = min(max(int(masked_m[g]), 0), M_cap)
+        if mm:
+            dense = oracle.gemm_nt(np.ascontiguousarray(a[g, :mm]),
+                                   np.ascontiguousarray(sfa[g]), np.ascontiguousarray(b[g]),
+                                   np.ascontiguousarray(sfb[g]), None)
+            assert np.array_equal(d[g, :mm], dense)
+        assert np.all(np.isnan(d[g, mm:]))
+    gs = np.repeat(np.arange(G), 3).astype(np.int32)
+    ms = np.tile(np.array([0, 1, 129]), G).astype(np.int32)
+    ns = np.tile(np.array([0, 33, 71]), G).astype(np.int32)
+    at = oracle.m_grouped_masked_at(a, sfa, b, sfb, None, masked_m, gs, ms, ns)
+    assert np.array_equal(np.isnan(at), np.isnan(d[gs, ms, ns]))
+    ok = ~np.isnan(at)
+    assert np.array_equal(at[ok], d[gs, ms, ns][ok])
+
+
+def test_masked_negative_count_is_zero_rows():
+    a = synth.random_codes(1, 0, (1, 8, 128))
+    b = synth.random_codes(1, 1, (1, 16, 128))
+    sfa = np.ones((1, 1, 8), dtype=np.float32)
+    sfb = np.ones((1, 1, 1), dtype=np.float32)
+    d = oracle.m_grouped_masked(a, sfa, b, sfb, None, np.array([-3], dtype=np.int32))
+    assert np.all(np.isnan(d))
