@@ -1,0 +1,167 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) FP8 block-scaled NT GEMM library.
+ *
+ * Operation (the "DeepGEMM" README summary on GeekNews, ja.news.hada.io topic
+ * 19459, section "GEMM interface and layout constraints"): D = C + A . B^T in
+ * the NT layout, A and B in FP8 E4M3, FP32 scaling factors with the LHS
+ * scales stored transposed, the caller doing the casting and transposition.
+ * Scales are applied during accumulation: for every 128-wide K block the FP8
+ * matrix-core partial is promoted into an FP32 accumulator after multiplying
+ * by sfa * sfb (two-level accumulation, "DeepSeek open-sources DeepGEMM",
+ * picoinsstore.com, paragraph on the Hopper design).  Granularity: one scale
+ * per row and 128-wide K block of A (1x128), one per 128x128 block of B.
+ *
+ *   D[m,n] = C[m,n] + sum_kb sfa[kb][m] * sfb[n/128][kb] * sum_{k in kb} A[m,k] B[n,k]
+ *
+ * Conventions for every entry point:
+ *  - Types: E4M3 values are uint8_t bit patterns (OCP E4M3FN: bias 7, no
+ *    infinities, max 448); bf16 values are uint16_t bit patterns; scales fp32.
+ *  - All tensors are dense, row-major (last index fastest), in device memory
+ *    owned by the caller; base pointers must be 16-byte aligned.  The library
+ *    keeps no pointer after the call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Argument errors are detected on the host and returned before
+ *    anything is launched; nothing is written then.  A failed launch returns
+ *    DG_ERR_HIP.  Device faults surface at the caller's next synchronisation.
+ *  - D is bf16, rounded to nearest even from the fp32 accumulator.  C is bf16
+ *    of the same shape as D, or NULL for C = 0; C may alias D exactly.
+ *  - K must be a positive multiple of 128.  M and N may be any positive size
+ *    (partial row and column tiles are handled).
+ *  - Dense calls with a small M use split-K: they keep an internal fp32
+ *    workspace per device and stream (allocated on first use, grown when a
+ *    larger problem arrives, freed at process exit).  Calls on one stream
+ *    are ordered; calls on different streams use different workspaces.
+ *  - Thread-safe: the only global settings are the CU cap and the last-config
+ *    string (which is per thread).
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_status {
+    DG_OK = 0,
+    DG_ERR_NULL = -1,        /* a required pointer is NULL */
+    DG_ERR_SHAPE = -2,       /* a size is out of range (K % 128, M, N, G <= 0, M_total % 128) */
+    DG_ERR_ALIGN = -3,       /* a pointer or leading dimension is misaligned */
+    DG_ERR_ARG = -4,         /* any other invalid argument */
+    DG_ERR_UNSUPPORTED = -5, /* valid but not supported here (e.g. not a gfx950 device) */
+    DG_ERR_HIP = -6          /* a HIP runtime call failed */
+} dg_status;
+
+/*
+ * Dense FP8 NT GEMM, D = C + A . B^T.
+ *   a   [M][K]                E4M3
+ *   sfa [K/128][ld_sfa]       fp32, sfa[kb*ld_sfa + m] scales A[m, 128kb : 128kb+128];
+ *                             ld_sfa >= M and ld_sfa % 4 == 0 (the transposed,
+ *                             16-byte aligned LHS scale layout); entries with
+ *                             m >= M are never used for results.
+ *   b   [N][K]                E4M3 (row n is column n of B^T)
+ *   sfb [ceil(N/128)][K/128]  fp32, sfb[nb*(K/128) + kb] scales the 128x128 block
+ *   c   [M][N] bf16 or NULL;  d [M][N] bf16 (written entirely).
+ * Errors: DG_ERR_NULL (a, sfa, b, sfb, d), DG_ERR_SHAPE (M, N < 1; K < 128 or
+ * K % 128), DG_ERR_ALIGN (ld_sfa < M or ld_sfa % 4; pointer not 16-B aligned).
+ */
+int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa,
+                   const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d,
+                   int M, int N, int K, void *stream);
+
+/*
+ * M-grouped contiguous layout ("DeepGEMM" README summary, section "Dense and
+ * Grouped GEMM"): the tokens of all experts are concatenated along M, N and K
+ * are shared, and every expert segment starts at a multiple of the M block
+ * (dg_get_mk_alignment_for_contiguous_layout(), 128 rows).
+ *   a   [M_total][K] E4M3;  sfa [K/128][M_total] fp32
+ *   b   [G][N][K] E4M3;     sfb [G][ceil(N/128)][K/128] fp32
+ *   c   [M_total][N] bf16 or NULL;  d [M_total][N] bf16
+ *   m_indices [M_total] int32 in device memory: the expert of each row, or -1
+ *             on padding rows.  Rows with -1 are neither computed nor written.
+ * Precondition (not checked on the device): each aligned 128-row block holds
+ * rows of at most one expert, valid rows first; ids are in [-1, G).
+ * Errors: DG_ERR_NULL, DG_ERR_SHAPE (M_total % 128, N, K, G < 1), DG_ERR_ALIGN.
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t *a, const float *sfa,
+                                        const uint8_t *b, const float *sfb,
+                                        const uint16_t *c, uint16_t *d,
+                                        const int32_t *m_indices,
+                                        int M_total, int N, int K, int G,
+                                        void *stream);
+
+/*
+ * M-grouped masked layout (same section): every group owns M_cap rows and
+ * only its first masked_m[g] rows are valid; the counts live on the device,
+ * so the host never reads them and the call is safe to capture in a graph.
+ *   a   [G][M_cap][K] E4M3;  sfa [G][K/128][round_up(M_cap,4)] fp32
+ *   b   [G][N][K] E4M3;      sfb [G][ceil(N/128)][K/128] fp32
+ *   c   [G][M_cap][N] bf16 or NULL;  d [G][M_cap][N] bf16
+ *   masked_m [G] int32 in device memory, clamped to [0, M_cap] on the device.
+ *   expected_m: host hint of the typical count (<= 0: unknown); it only
+ *               steers the tile choice and never changes results.
+ * Rows r >= masked_m[g] of d are left untouched.
+ * Errors: DG_ERR_NULL, DG_ERR_SHAPE (G, M_cap, N < 1; K), DG_ERR_ALIGN.
+ */
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t *a, const float *sfa,
+                                    const uint8_t *b, const float *sfb,
+                                    const uint16_t *c, uint16_t *d,
+                                    const int32_t *masked_m,
+                                    int G, int M_cap, int N, int K,
+                                    int expected_m, void *stream);
+
+/*
+ * E4M3 quantiser, one scale per row and 128-wide K block (the LHS layout):
+ *   x [groups][rows][K] fp32  ->  q [groups][rows][K] E4M3,
+ *   sf [groups][K/128][ld_sf] fp32 with sf = max(amax, 1e-4) / 448 (one IEEE
+ *   fp32 division) and q = round-to-nearest-even(x / sf) (IEEE division,
+ *   saturating at +-448).  Entries of sf with row >= rows are not written.
+ * The pages leave the cast to the user ("GEMM interface and layout
+ * constraints"); this kernel writes the required scale layout directly.
+ * Errors: DG_ERR_NULL, DG_ERR_SHAPE (groups, rows < 1; K), DG_ERR_ALIGN
+ * (ld_sf < rows or ld_sf % 4).
+ */
+int dg_quantize_e4m3_1x128(const float *x, int groups, int rows, int K,
+                           uint8_t *q, float *sf, int ld_sf, void *stream);
+
+/*
+ * E4M3 quantiser, one scale per 128x128 block (the RHS layout):
+ *   x [groups][rows][K] -> q, sf [groups][ceil(rows/128)][K/128].
+ * The last row block of each group may be partial; blocks never straddle
+ * groups.  Same scale formula and rounding as the 1x128 quantiser.
+ */
+int dg_quantize_e4m3_128x128(const float *x, int groups, int rows, int K,
+                             uint8_t *q, float *sf, void *stream);
+
+/* Row alignment of expert segments in the contiguous layout (128).  The
+ * setter accepts only 128 and returns DG_ERR_ARG otherwise. ("Utilities and
+ * environment variables" section.) */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+int dg_set_mk_alignment_for_contiguous_layout(int alignment);
+
+/* Leading dimension for a transposed scale array over mn rows: round_up(mn, 4)
+ * (16-byte aligned columns, the analogue of the TMA-aligned size). */
+int dg_get_sf_aligned_size(int mn);
+
+/* Cap on the number of compute units the tile scheduler plans for (the
+ * analogue of set_num_sms).  n >= 1 sets the cap, n == 0 restores the
+ * device's CU count; negative -> DG_ERR_ARG.  get returns the cap in force
+ * (the device's CU count when none is set, or a negative dg_status when no
+ * device can be queried). */
+int dg_set_num_cus(int n);
+int dg_get_num_cus(void);
+
+/* Static string for a status code. */
+const char *dg_status_string(int status);
+
+/* Description of the kernel configuration chosen by this thread's last GEMM
+ * call (family, tile, grid, split).  Also printed to stderr for every call
+ * when the environment variable DG_PRINT_CONFIGS is set to a non-zero value. */
+const char *dg_last_config(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -1,0 +1,203 @@
+"""ctypes binding of libdg.so (C ABI in include/dg.h).
+
+Argument marshalling only: the functions check that tensors have the dtype,
+device, contiguity and shape the C ABI documents, then pass raw device
+pointers, sizes and the current HIP stream.  Every step of the computation
+runs in the library's HIP kernels.  There is no fallback: if libdg.so is
+missing, loading raises.
+
+E4M3 tensors may be torch.uint8 or torch.float8_e4m3fn; bf16 tensors are
+torch.bfloat16; scales torch.float32; index tensors torch.int32.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+DG_OK = 0
+_STATUS = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_ALIGN", -4: "DG_ERR_ARG",
+           -5: "DG_ERR_UNSUPPORTED", -6: "DG_ERR_HIP"}
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "dg_fp8_gemm_nt": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                  ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                       ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int,
+                                                       ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_m_grouped_fp8_gemm_nt_masked": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                   ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int,
+                                                   ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_quantize_e4m3_1x128": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p,
+                                          ct.c_int, ct.c_void_p]),
+    "dg_quantize_e4m3_128x128": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p,
+                                            ct.c_void_p]),
+    "dg_get_mk_alignment_for_contiguous_layout": (ct.c_int, []),
+    "dg_set_mk_alignment_for_contiguous_layout": (ct.c_int, [ct.c_int]),
+    "dg_get_sf_aligned_size": (ct.c_int, [ct.c_int]),
+    "dg_set_num_cus": (ct.c_int, [ct.c_int]),
+    "dg_get_num_cus": (ct.c_int, []),
+    "dg_status_string": (ct.c_char_p, [ct.c_int]),
+    "dg_last_config": (ct.c_char_p, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({lib().dg_status_string(status).decode()})")
+
+
+def lib() -> ct.CDLL:
+    """The loaded libdg.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                                      "`python -m moe_grouped_gemm_scaled_amd.build`")
+                l = ct.CDLL(LIB_PATH)
+                for name, (res, args) in EXPORTS.items():
+                    f = getattr(l, name)
+                    f.restype = res
+                    f.argtypes = args
+                _lib = l
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != DG_OK:
+        raise DGError(status, where)
+
+
+def _stream(t: torch.Tensor):
+    return ct.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _ptr(t, dtypes, name, shape=None):
+    if t is None:
+        return None
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ct.c_void_p(t.data_ptr())
+
+
+def ceil_div(a: int, b: int) -> int:
+    return (a + b - 1) // b
+
+
+def fp8_gemm_nt(a, sfa, b, sfb, d, c=None):
+    """D = C + A . B^T.  a[M,K], sfa[K/128, ld_sfa], b[N,K], sfb[ceil(N/128), K/128], d/c[M,N] bf16."""
+    M, K = a.shape
+    N = b.shape[0]
+    if sfa.dim() != 2 or sfa.shape[0] != K // 128:
+        raise ValueError(f"sfa: shape {tuple(sfa.shape)}, expected [K/128={K // 128}, ld_sfa]")
+    args = (_ptr(a, _FP8, "a", (M, K)), _ptr(sfa, torch.float32, "sfa"), int(sfa.shape[1]),
+            _ptr(b, _FP8, "b", (N, K)), _ptr(sfb, torch.float32, "sfb", (ceil_div(N, 128), K // 128)),
+            _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
+    _check(lib().dg_fp8_gemm_nt(*args), "dg_fp8_gemm_nt")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, m_indices, c=None):
+    """a[M_total,K], sfa[K/128, M_total], b[G,N,K], sfb[G, ceil(N/128), K/128], d/c[M_total,N], m_indices[M_total]."""
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    args = (_ptr(a, _FP8, "a", (M_total, K)), _ptr(sfa, torch.float32, "sfa", (K // 128, M_total)),
+            _ptr(b, _FP8, "b", (G, N, K)), _ptr(sfb, torch.float32, "sfb", (G, ceil_div(N, 128), K // 128)),
+            _ptr(c, torch.bfloat16, "c", (M_total, N)), _ptr(d, torch.bfloat16, "d", (M_total, N)),
+            _ptr(m_indices, torch.int32, "m_indices", (M_total,)), M_total, N, K, G, _stream(d))
+    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous(*args), "dg_m_grouped_fp8_gemm_nt_contiguous")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, c=None):
+    """a[G,M_cap,K], sfa[G, K/128, round_up(M_cap,4)], b[G,N,K], sfb[G, ceil(N/128), K/128], d/c[G,M_cap,N]."""
+    G, M_cap, K = a.shape
+    N = b.shape[1]
+    ld = (M_cap + 3) // 4 * 4
+    args = (_ptr(a, _FP8, "a", (G, M_cap, K)), _ptr(sfa, torch.float32, "sfa", (G, K // 128, ld)),
+            _ptr(b, _FP8, "b", (G, N, K)), _ptr(sfb, torch.float32, "sfb", (G, ceil_div(N, 128), K // 128)),
+            _ptr(c, torch.bfloat16, "c", (G, M_cap, N)), _ptr(d, torch.bfloat16, "d", (G, M_cap, N)),
+            _ptr(masked_m, torch.int32, "masked_m", (G,)), G, M_cap, N, K, int(expected_m), _stream(d))
+    _check(lib().dg_m_grouped_fp8_gemm_nt_masked(*args), "dg_m_grouped_fp8_gemm_nt_masked")
+    return d
+
+
+def quantize_e4m3_1x128(x, q=None, sf=None, ld_sf=None):
+    """x[groups, rows, K] or [rows, K] fp32 -> (q uint8, sf[groups, K/128, ld_sf] or [K/128, ld_sf])."""
+    squeeze = x.dim() == 2
+    groups, rows, K = (1,) + tuple(x.shape) if squeeze else tuple(x.shape)
+    ld = (rows + 3) // 4 * 4 if ld_sf is None else int(ld_sf)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.zeros((K // 128, ld) if squeeze else (groups, K // 128, ld), dtype=torch.float32, device=x.device)
+    _ptr(sf, torch.float32, "sf", (K // 128, ld) if squeeze else (groups, K // 128, ld))
+    args = (_ptr(x, torch.float32, "x"), groups, rows, K, _ptr(q, _FP8, "q", tuple(x.shape)),
+            ct.c_void_p(sf.data_ptr()), ld, _stream(x))
+    _check(lib().dg_quantize_e4m3_1x128(*args), "dg_quantize_e4m3_1x128")
+    return q, sf
+
+
+def quantize_e4m3_128x128(x, q=None, sf=None):
+    """x[groups, rows, K] or [rows, K] fp32 -> (q uint8, sf[groups, ceil(rows/128), K/128])."""
+    squeeze = x.dim() == 2
+    groups, rows, K = (1,) + tuple(x.shape) if squeeze else tuple(x.shape)
+    shape_sf = (ceil_div(rows, 128), K // 128) if squeeze else (groups, ceil_div(rows, 128), K // 128)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty(shape_sf, dtype=torch.float32, device=x.device)
+    args = (_ptr(x, torch.float32, "x"), groups, rows, K, _ptr(q, _FP8, "q", tuple(x.shape)),
+            _ptr(sf, torch.float32, "sf", shape_sf), _stream(x))
+    _check(lib().dg_quantize_e4m3_128x128(*args), "dg_quantize_e4m3_128x128")
+    return q, sf
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return lib().dg_get_mk_alignment_for_contiguous_layout()
+
+
+def set_mk_alignment_for_contiguous_layout(alignment: int):
+    _check(lib().dg_set_mk_alignment_for_contiguous_layout(int(alignment)), "dg_set_mk_alignment_for_contiguous_layout")
+
+
+def get_sf_aligned_size(mn: int) -> int:
+    return lib().dg_get_sf_aligned_size(int(mn))
+
+
+def set_num_cus(n: int):
+    _check(lib().dg_set_num_cus(int(n)), "dg_set_num_cus")
+
+
+def get_num_cus() -> int:
+    v = lib().dg_get_num_cus()
+    if v < 0:
+        raise DGError(v, "dg_get_num_cus")
+    return v
+
+
+def last_config() -> str:
+    return lib().dg_last_config().decode()

@@ -1,0 +1,171 @@
+// api.cpp -- the C ABI declared in include/dg.h: argument validation on the
+// host (before any HIP call), device checks, kernel dispatch, and the small
+// utility entry points.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <string>
+
+#include "../../include/dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_cap{0};                  // 0: use the device's CU count
+std::atomic<int> g_dev_cus[kMaxDevices];       // 0: not queried yet
+std::atomic<int> g_dev_ok[kMaxDevices];        // 0 unknown, 1 gfx950, -1 other
+thread_local std::string t_last_config;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool print_configs() {
+    static const int v = [] {
+        const char *e = getenv("DG_PRINT_CONFIGS");
+        return (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+    }();
+    return v != 0;
+}
+
+// Current device, checked to be gfx950; fills its CU count.
+int current_device(int &dev, int &cus) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DG_ERR_HIP;
+    int ok = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (ok == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DG_ERR_HIP;
+        ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        g_dev_ok[dev].store(ok, std::memory_order_relaxed);
+    }
+    if (ok < 0) return DG_ERR_UNSUPPORTED;
+    cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+    const int cap = g_cu_cap.load(std::memory_order_relaxed);
+    if (cap > 0 && cap < cus) cus = cap;
+    return DG_OK;
+}
+
+int run_gemm(const dg::GemmProblem &p, void *stream) {
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) return st;
+    std::string cfg;
+    const hipError_t err = dg::launch_gemm(p, cus, static_cast<hipStream_t>(stream), cfg);
+    t_last_config = cfg;
+    if (print_configs()) fprintf(stderr, "[dg] %s\n", cfg.c_str());
+    return err == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
+int check_k(int K) { return (K < 128 || K % 128 != 0) ? DG_ERR_SHAPE : DG_OK; }
+
+}  // namespace
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    if (!a || !sfa || !b || !sfb || !d) return DG_ERR_NULL;
+    if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if (ld_sfa < M || ld_sfa % 4 != 0) return DG_ERR_ALIGN;
+    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+        (c && !aligned16(c)))
+        return DG_ERR_ALIGN;
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0};
+    return run_gemm(p, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                                        const uint16_t *c, uint16_t *d, const int32_t *m_indices, int M_total,
+                                        int N, int K, int G, void *stream) {
+    if (!a || !sfa || !b || !sfb || !d || !m_indices) return DG_ERR_NULL;
+    if (M_total < 1 || M_total % 128 != 0 || N < 1 || G < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+        !aligned16(m_indices) || (c && !aligned16(c)))
+        return DG_ERR_ALIGN;
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, m_indices, M_total, N, K, M_total, G, dg::Mode::Contig, 0};
+    return run_gemm(p, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                                    const uint16_t *c, uint16_t *d, const int32_t *masked_m, int G, int M_cap,
+                                    int N, int K, int expected_m, void *stream) {
+    if (!a || !sfa || !b || !sfb || !d || !masked_m) return DG_ERR_NULL;
+    if (G < 1 || M_cap < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+        (c && !aligned16(c)))
+        return DG_ERR_ALIGN;
+    const int ld = (M_cap + 3) / 4 * 4;
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, masked_m, M_cap, N, K, ld, G, dg::Mode::Masked, expected_m};
+    return run_gemm(p, stream);
+}
+
+int dg_quantize_e4m3_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, int ld_sf,
+                           void *stream) {
+    if (!x || !q || !sf) return DG_ERR_NULL;
+    if (groups < 1 || rows < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if (ld_sf < rows || ld_sf % 4 != 0) return DG_ERR_ALIGN;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return DG_ERR_ALIGN;
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) return st;
+    return dg::launch_quant_1x128(x, groups, rows, K, q, sf, ld_sf, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? DG_OK
+               : DG_ERR_HIP;
+}
+
+int dg_quantize_e4m3_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, void *stream) {
+    if (!x || !q || !sf) return DG_ERR_NULL;
+    if (groups < 1 || rows < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return DG_ERR_ALIGN;
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) return st;
+    return dg::launch_quant_128x128(x, groups, rows, K, q, sf, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? DG_OK
+               : DG_ERR_HIP;
+}
+
+int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+int dg_set_mk_alignment_for_contiguous_layout(int alignment) { return alignment == 128 ? DG_OK : DG_ERR_ARG; }
+
+int dg_get_sf_aligned_size(int mn) { return mn <= 0 ? 0 : (mn + 3) / 4 * 4; }
+
+int dg_set_num_cus(int n) {
+    if (n < 0) return DG_ERR_ARG;
+    g_cu_cap.store(n, std::memory_order_relaxed);
+    return DG_OK;
+}
+
+int dg_get_num_cus(void) {
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) {
+        const int cap = g_cu_cap.load(std::memory_order_relaxed);
+        return cap > 0 ? cap : st;
+    }
+    return cus;
+}
+
+const char *dg_status_string(int status) {
+    switch (status) {
+    case DG_OK: return "DG_OK";
+    case DG_ERR_NULL: return "DG_ERR_NULL: a required pointer is NULL";
+    case DG_ERR_SHAPE: return "DG_ERR_SHAPE: a size is out of range";
+    case DG_ERR_ALIGN: return "DG_ERR_ALIGN: a pointer or leading dimension is misaligned";
+    case DG_ERR_ARG: return "DG_ERR_ARG: invalid argument";
+    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED: not supported on this device";
+    case DG_ERR_HIP: return "DG_ERR_HIP: a HIP runtime call failed";
+    default: return "unknown dg_status";
+    }
+}
+
+const char *dg_last_config(void) { return t_last_config.c_str(); }
+
+}  // extern "C"

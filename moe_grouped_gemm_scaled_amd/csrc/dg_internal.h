@@ -1,0 +1,38 @@
+// dg_internal.h -- host-side declarations shared by the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace dg {
+
+hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
+                              int ld_sf, hipStream_t stream);
+hipError_t launch_quant_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
+                                hipStream_t stream);
+
+enum class Mode : int { Dense = 0, Contig = 1, Masked = 2 };
+
+// Arguments of one GEMM launch.  Per group, A has `rows_a` rows (dense: M,
+// contiguous: M_total, masked: M_cap) and its scales have leading dimension
+// `ld_sfa`; `idx` is m_indices (contiguous) or masked_m (masked).
+struct GemmProblem {
+    const uint8_t *a;
+    const float *sfa;
+    const uint8_t *b;
+    const float *sfb;
+    const uint16_t *c;
+    uint16_t *d;
+    const int32_t *idx;
+    int rows_a, N, K, ld_sfa, G;
+    Mode mode;
+    int expected_m;   // masked only: host hint, <= 0 unknown
+};
+
+// Chooses a kernel configuration, launches it on `stream`, and describes the
+// choice in `config`.  Returns the HIP error of the launch.
+hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
+
+}  // namespace dg

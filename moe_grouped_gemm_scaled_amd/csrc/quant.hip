@@ -1,0 +1,137 @@
+// quant.hip -- fp32 -> E4M3FN block quantisers for gfx950.
+//
+// One scale per block, sf = max(amax, 1e-4) / 448 (448 is the largest E4M3FN
+// magnitude); every element is divided by sf with an IEEE fp32 division and
+// rounded to the nearest E4M3FN value, ties to the even code, saturating at
+// +-448.  Block shapes: 1x128 (activations, scales written K-block-major,
+// i.e. transposed) and 128x128 (weights).  The FP8 GEMM interface on the
+// "DeepGEMM" README summary (GeekNews, "GEMM interface and layout
+// constraints") leaves this cast to the caller; these kernels write the
+// scale layouts that the GEMM entry points read.
+//
+// Both kernels are HBM-bound: 4 bytes read and 1 byte written per element.
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+
+// Round |v| (finite, < 448) to the E4M3FN grid, nearest with ties to even.
+// Normal range [2^-6, 448): keep 3 of the 23 fp32 mantissa bits with an
+// integer round-half-even on the dropped 20 bits (a carry moves into the
+// exponent, as it should).  Subnormal range [0, 2^-6): the grid step is 2^-9,
+// so the code is rint(|v| * 2^9) (exact scaling, rint ties to even), and 8
+// becomes code 0x08 = 2^-6, the smallest normal.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t mag = u & 0x7fffffffu;
+    if (mag > 0x7f800000u) return 0x7fu;                  // NaN
+    const float a = __uint_as_float(mag);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7eu;                                      // saturate (also +-inf)
+    } else if (a < 0.015625f) {                            // 2^-6
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        const uint32_t r = mag + 0x7ffffu + ((mag >> 20) & 1u);
+        const uint32_t e = (r >> 23) - 127u + 7u;          // biased E4M3 exponent, 1..15
+        code = (e << 3) | ((r >> 20) & 7u);
+    }
+    return sign | code;
+}
+
+__device__ __forceinline__ float block_scale(float amax) {
+    return fmaxf(amax, 1e-4f) / 448.0f;                   // IEEE division (no fast-math)
+}
+
+// 1x128: a half-wave (32 lanes x float4) per 128-element block; consecutive
+// half-waves take consecutive blocks of a row, so loads and stores coalesce.
+__global__ void __launch_bounds__(256)
+quant_1x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ sf,
+                   int rows, int nkb, int ld_sf, int64_t nblocks) {
+    const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int l = threadIdx.x & 31;
+    if (blk >= nblocks) return;
+    const float4 v = reinterpret_cast<const float4 *>(x + blk * kKBlock)[l];
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    const float s = block_scale(amax);
+    const uint32_t packed = e4m3_encode(v.x / s) | (e4m3_encode(v.y / s) << 8) |
+                            (e4m3_encode(v.z / s) << 16) | (e4m3_encode(v.w / s) << 24);
+    reinterpret_cast<uint32_t *>(q + blk * kKBlock)[l] = packed;
+    if (l == 0) {
+        const int64_t row_all = blk / nkb;                 // g * rows + r
+        const int kb = (int)(blk - row_all * nkb);
+        const int64_t g = row_all / rows;
+        const int r = (int)(row_all - g * rows);
+        sf[(g * nkb + kb) * (int64_t)ld_sf + r] = s;
+    }
+}
+
+// 128x128: one 256-thread workgroup per block.  Thread t covers rows
+// t/32 + 8i (i < 16) at column chunk t%32, keeping its 64 values in registers
+// between the amax reduction and the encode.
+__global__ void __launch_bounds__(256)
+quant_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ sf,
+                     int rows, int K, int nrb, int nkb) {
+    const int kb = blockIdx.x % nkb;
+    const int rb = (blockIdx.x / nkb) % nrb;
+    const int64_t g = blockIdx.x / ((int64_t)nkb * nrb);
+    const int t = threadIdx.x;
+    const int r0 = rb * 128;
+    const int col = kb * kKBlock + (t & 31) * 4;
+    const float *xg = x + g * rows * (int64_t)K;
+    float4 v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = r0 + (t >> 5) + 8 * i;
+        if (r < rows) {
+            v[i] = *reinterpret_cast<const float4 *>(xg + (int64_t)r * K + col);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    __shared__ float wmax[4];
+    if ((t & 63) == 0) wmax[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s = block_scale(amax);
+    uint8_t *qg = q + g * rows * (int64_t)K;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = r0 + (t >> 5) + 8 * i;
+        if (r < rows) {
+            const uint32_t packed = e4m3_encode(v[i].x / s) | (e4m3_encode(v[i].y / s) << 8) |
+                                    (e4m3_encode(v[i].z / s) << 16) | (e4m3_encode(v[i].w / s) << 24);
+            *reinterpret_cast<uint32_t *>(qg + (int64_t)r * K + col) = packed;
+        }
+    }
+    if (t == 0) sf[(g * nrb + rb) * (int64_t)nkb + kb] = s;
+}
+
+hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
+                              int ld_sf, hipStream_t stream) {
+    const int nkb = K / kKBlock;
+    const int64_t nblocks = (int64_t)groups * rows * nkb;
+    const int64_t grid = (nblocks + 7) / 8;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_1x128_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       x, q, sf, rows, nkb, ld_sf, nblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
+                                hipStream_t stream) {
+    const int nkb = K / kKBlock;
+    const int nrb = (rows + 127) / 128;
+    const int64_t grid = (int64_t)groups * nrb * nkb;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_128x128_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       x, q, sf, rows, K, nrb, nkb);
+    return hipGetLastError();
+}
+
+}  // namespace dg

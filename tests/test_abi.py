@@ -1,0 +1,110 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/dg.h declares, and rejects invalid arguments on the host before
+any HIP call (so these calls never reach the device)."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+from moe_grouped_gemm_scaled_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+# Fake, 16-byte aligned, never dereferenced: validation fails before use.
+P = ct.c_void_p(0x10000)
+MIS = ct.c_void_p(0x10004)
+NULL = None
+S = None    # default stream
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from moe_grouped_gemm_scaled_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.EXPORTS), set(names) ^ set(binding.EXPORTS)
+
+
+def test_utilities(lib):
+    assert lib.dg_get_mk_alignment_for_contiguous_layout() == 128
+    assert lib.dg_set_mk_alignment_for_contiguous_layout(128) == 0
+    assert lib.dg_set_mk_alignment_for_contiguous_layout(64) == -4
+    assert [lib.dg_get_sf_aligned_size(x) for x in (1, 4, 5, 128, 130)] == [4, 4, 8, 128, 132]
+    assert lib.dg_set_num_cus(-1) == -4
+    assert lib.dg_set_num_cus(0) == 0
+    for s in range(-6, 1):
+        assert lib.dg_status_string(s).decode().startswith(("DG_OK", "DG_ERR"))
+
+
+def test_dense_argument_errors(lib):
+    f = lib.dg_fp8_gemm_nt
+    # a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream
+    assert f(NULL, P, 64, P, P, NULL, P, 64, 64, 128, S) == -1
+    assert f(P, P, 64, P, P, NULL, NULL, 64, 64, 128, S) == -1
+    assert f(P, P, 64, P, P, NULL, P, 64, 64, 100, S) == -2       # K % 128
+    assert f(P, P, 64, P, P, NULL, P, 64, 64, 0, S) == -2
+    assert f(P, P, 64, P, P, NULL, P, 0, 64, 128, S) == -2        # M < 1
+    assert f(P, P, 64, P, P, NULL, P, 64, 0, 128, S) == -2        # N < 1
+    assert f(P, P, 60, P, P, NULL, P, 64, 64, 128, S) == -3       # ld_sfa < M
+    assert f(P, P, 66, P, P, NULL, P, 65, 64, 128, S) == -3       # ld_sfa % 4
+    assert f(MIS, P, 64, P, P, NULL, P, 64, 64, 128, S) == -3     # misaligned a
+    assert f(P, P, 64, P, P, MIS, P, 64, 64, 128, S) == -3        # misaligned c
+
+
+def test_contiguous_argument_errors(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    # a, sfa, b, sfb, c, d, m_indices, M_total, N, K, G, stream
+    assert f(P, P, P, P, NULL, P, NULL, 128, 64, 128, 2, S) == -1
+    assert f(P, P, P, P, NULL, P, P, 100, 64, 128, 2, S) == -2     # M_total % 128
+    assert f(P, P, P, P, NULL, P, P, 128, 64, 128, 0, S) == -2     # G < 1
+    assert f(P, P, P, P, NULL, P, P, 128, 64, 129, 2, S) == -2
+    assert f(P, P, P, P, NULL, P, MIS, 128, 64, 128, 2, S) == -3
+
+
+def test_masked_argument_errors(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_masked
+    # a, sfa, b, sfb, c, d, masked_m, G, M_cap, N, K, expected_m, stream
+    assert f(P, P, P, P, NULL, P, NULL, 2, 64, 64, 128, 0, S) == -1
+    assert f(P, P, P, P, NULL, P, P, 0, 64, 64, 128, 0, S) == -2
+    assert f(P, P, P, P, NULL, P, P, 2, 0, 64, 128, 0, S) == -2
+    assert f(P, P, P, P, NULL, P, P, 2, 64, 64, 64, 0, S) == -2
+    assert f(P, MIS, P, P, NULL, P, P, 2, 64, 64, 128, 0, S) == -3
+
+
+def test_quantiser_argument_errors(lib):
+    f1 = lib.dg_quantize_e4m3_1x128
+    # x, groups, rows, K, q, sf, ld_sf, stream
+    assert f1(NULL, 1, 4, 128, P, P, 4, S) == -1
+    assert f1(P, 1, 4, 130, P, P, 4, S) == -2
+    assert f1(P, 0, 4, 128, P, P, 4, S) == -2
+    assert f1(P, 1, 5, 128, P, P, 6, S) == -3
+    assert f1(P, 1, 5, 128, P, P, 4, S) == -3
+    f2 = lib.dg_quantize_e4m3_128x128
+    assert f2(P, 1, 4, 128, NULL, P, S) == -1
+    assert f2(P, 1, 0, 128, P, P, S) == -2
+    assert f2(P, 1, 4, 128, MIS, P, S) == -3
+
+
+def test_binding_rejects_wrong_tensors_on_host():
+    import torch
+    a = torch.zeros((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        binding._ptr(a, torch.uint8, "a")     # not a device tensor
+    with pytest.raises(TypeError):
+        binding._ptr(a, torch.float32, "a")
