@@ -1,0 +1,389 @@
+"""Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|contiguous|masked|small]
+
+A step is one pass of the hot path over one batch of synthetic input: for
+every GEMM of the workload, quantise the fp32 activations (1x128 scales) and
+run the FP8 block-scaled GEMM.  Weights are quantised once (128x128 scales)
+before timing, as in inference.  Default workload: the decode-shaped dense
+GEMMs, M in {64, 128} x (N, K) in {(2112, 7168), (24576, 1536), (7168, 16384)},
+C = 0, bf16 D.
+
+Timing: each distinct step is captured once in a HIP graph (so host launch
+cost does not stall the GPU) and the timed region replays exactly K steps,
+bracketed by device synchronisation.  Weight copies rotate so that every B
+is re-read only after more than 512 MB of other traffic (the 256 MB
+Infinity Cache cannot serve it).  Per-kernel durations for the roofline are
+measured separately with HIP events around graph replays of one GEMM launch
+repeated over rotating weight copies.
+
+Prints ONE JSON line.  `value` is whole-job throughput: decode -> GB/s of
+algorithmic HBM traffic (activation read + codes/scales written by the
+quantiser, A + B + scales + D read/written by the GEMM); prefill and grouped
+-> TFLOP/s of 2*M_valid*N*K.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from moe_grouped_gemm_scaled_amd import binding as dg  # noqa: E402
+from moe_grouped_gemm_scaled_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
+MALL_BYTES = 256 << 20
+ROTATE_BYTES = 512 << 20
+
+METRIC = "FP8 GEMM TFLOPS (prefill) and HBM GB/s (decode) as % of MI355X peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def gemm_bytes(m_valid, N, K, g_active=1, with_c=False):
+    """Algorithmic bytes of one GEMM: A + B + sfa + sfb + D (+ C), valid rows only."""
+    nkb = K // 128
+    b = m_valid * K + g_active * N * K + 4 * m_valid * nkb + 4 * g_active * cdiv(N, 128) * nkb + 2 * m_valid * N
+    if with_c:
+        b += 2 * m_valid * N
+    return b
+
+
+def quant_bytes(rows, K):
+    """fp32 read + E4M3 written + one fp32 scale per 128 elements."""
+    return rows * K * 4 + rows * K + 4 * rows * (K // 128)
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+class Job:
+    """One GEMM of a step: activation quantiser + GEMM, with rotating weight copies."""
+
+    def __init__(self, name, launch, copies, flops, bytes_gemm, bytes_quant):
+        self.name = name
+        self.launch = launch          # launch(copy_index, with_quant) -> None
+        self.copies = copies
+        self.flops = flops
+        self.bytes_gemm = bytes_gemm
+        self.bytes_quant = bytes_quant
+
+
+def n_copies(weight_bytes):
+    return max(2, cdiv(ROTATE_BYTES, max(1, weight_bytes)) + 1)
+
+
+def make_weights(G, N, K, seed):
+    xb = torch.from_numpy(synth.normal_f32(seed, synth.STREAM_B, (G, N, K))).cuda()
+    b, sfb = dg.quantize_e4m3_128x128(xb)
+    del xb
+    return b, sfb
+
+
+def replicate(t, n):
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+def dense_jobs(cfgs):
+    jobs = []
+    weights = {}
+    for cfg in cfgs:
+        M, N, K, seed = cfg["M"], cfg["N"], cfg["K"], cfg["seed"]
+        key = (M, N, K)           # no sharing between jobs: every GEMM streams its own copies
+        if key not in weights:
+            b, sfb = make_weights(1, N, K, seed)
+            nc = n_copies(N * K)
+            weights[key] = (replicate(b[0], nc), replicate(sfb[0], nc))
+        bs, sfbs = weights[key]
+        x = torch.from_numpy(synth.normal_f32(seed, synth.STREAM_A, (M, K))).cuda()
+        a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        sfa = torch.zeros((K // 128, dg.get_sf_aligned_size(M)), dtype=torch.float32, device="cuda")
+        c = None
+        if cfg["with_c"]:
+            c = torch.from_numpy(synth.normal_bf16_bits(seed, synth.STREAM_C, (M, N)).view(np.int16)).cuda()
+            c = c.view(torch.bfloat16)
+        d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def launch(ci, with_quant, x=x, a=a, sfa=sfa, bs=bs, sfbs=sfbs, c=c, d=d):
+            if with_quant:
+                dg.quantize_e4m3_1x128(x, q=a, sf=sfa)
+            dg.fp8_gemm_nt(a, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c)
+
+        jobs.append(Job(cfg["name"], launch, len(bs), 2.0 * M * N * K,
+                        gemm_bytes(M, N, K, with_c=cfg["with_c"]), quant_bytes(M, K)))
+    return jobs
+
+
+def contiguous_jobs():
+    cfg = synth.CONTIGUOUS
+    counts = synth.contiguous_counts(cfg)
+    m_idx = synth.contiguous_m_indices(counts)
+    M_total, N, K, G = m_idx.size, cfg["N"], cfg["K"], cfg["G"]
+    b, sfb = make_weights(G, N, K, cfg["seed"])
+    nc = n_copies(G * N * K)
+    bs, sfbs = replicate(b, nc), replicate(sfb, nc)
+    x = torch.from_numpy(synth.normal_f32(cfg["seed"], synth.STREAM_A, (M_total, K))).cuda()
+    a = torch.empty((M_total, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.zeros((K // 128, M_total), dtype=torch.float32, device="cuda")
+    mi = torch.from_numpy(m_idx).cuda()
+    d = torch.empty((M_total, N), dtype=torch.bfloat16, device="cuda")
+    m_valid = int(counts.sum())
+
+    def launch(ci, with_quant):
+        if with_quant:
+            dg.quantize_e4m3_1x128(x, q=a, sf=sfa)
+        dg.m_grouped_fp8_gemm_nt_contiguous(a, sfa, bs[ci % nc], sfbs[ci % nc], d, mi)
+
+    return [Job(cfg["name"], launch, nc, 2.0 * m_valid * N * K, gemm_bytes(m_valid, N, K, G),
+                quant_bytes(M_total, K))], dict(counts=counts.tolist(), M_total=M_total, m_valid=m_valid)
+
+
+def masked_jobs():
+    cfg = synth.MASKED
+    mm = synth.masked_counts(cfg)
+    G, M_cap, N, K = cfg["G"], cfg["M_cap"], cfg["N"], cfg["K"]
+    b, sfb = make_weights(G, N, K, cfg["seed"])
+    g_active = int((mm > 0).sum())
+    nc = n_copies(g_active * N * K)
+    bs, sfbs = replicate(b, nc), replicate(sfb, nc)
+    x = torch.from_numpy(synth.normal_f32(cfg["seed"], synth.STREAM_A, (G, M_cap, K))).cuda()
+    a = torch.empty((G, M_cap, K), dtype=torch.uint8, device="cuda")
+    sfa = torch.zeros((G, K // 128, dg.get_sf_aligned_size(M_cap)), dtype=torch.float32, device="cuda")
+    mmt = torch.from_numpy(mm).cuda()
+    d = torch.empty((G, M_cap, N), dtype=torch.bfloat16, device="cuda")
+    m_valid = int(mm.sum())
+
+    def launch(ci, with_quant):
+        if with_quant:
+            dg.quantize_e4m3_1x128(x, q=a, sf=sfa)
+        dg.m_grouped_fp8_gemm_nt_masked(a, sfa, bs[ci % nc], sfbs[ci % nc], d, mmt, expected_m=M_cap // 2)
+
+    # the activation quantiser runs over the whole padded buffer (counts live on the device)
+    return [Job(cfg["name"], launch, nc, 2.0 * m_valid * N * K, gemm_bytes(m_valid, N, K, g_active),
+                quant_bytes(G * M_cap, K))], dict(masked_m=mm.tolist(), m_valid=m_valid, g_active=g_active)
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def capture(fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                         # warm: first-call allocations happen outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def kernel_durations(jobs, reps=24):
+    """Average duration of one GEMM launch per job: HIP events around graph
+    replays of `reps` launches over rotating weight copies (quantiser excluded)."""
+    out = []
+    for j in jobs:
+        def body(j=j):
+            for r in range(reps):
+                j.launch(r, False)
+        g = capture(body)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(5):
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            best = ms if best is None else min(best, ms)
+        out.append(best)
+        del g
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(workload, jobs_meta, budget_s=15.0):
+    import oracle
+    cores = oracle.num_threads()
+    if workload != "decode":
+        return None
+    total_bytes = 0
+    t_full = 0.0
+    macs_sample = 0
+    cfgs = synth.DECODE
+    # calibrate the oracle's multiply-add rate on a small slice
+    cfg = cfgs[0]
+    xa = synth.normal_f32(cfg["seed"], synth.STREAM_A, (cfg["M"], cfg["K"]))
+    xb = synth.normal_f32(cfg["seed"], synth.STREAM_B, (256, cfg["K"]))
+    a, sfa = oracle.quantize_1x128(xa)
+    b, sfb = oracle.quantize_128x128(xb)
+    t0 = time.perf_counter()
+    oracle.gemm_nt(a, sfa, b[:64], sfb[:1], None)
+    rate = cfg["M"] * 64 * cfg["K"] / (time.perf_counter() - t0)
+    full_macs = sum(c["M"] * c["N"] * c["K"] for c in cfgs)
+    frac = min(1.0, budget_s * rate / full_macs)
+    for cfg in cfgs:
+        M, N, K = cfg["M"], cfg["N"], cfg["K"]
+        ns = max(128, int(N * frac) // 128 * 128)
+        xa = synth.normal_f32(cfg["seed"], synth.STREAM_A, (M, K))
+        xb = synth.normal_f32(cfg["seed"], synth.STREAM_B, (ns, K))
+        b, sfb = oracle.quantize_128x128(xb)                  # weights: offline, not timed
+        t0 = time.perf_counter()
+        a, sfa = oracle.quantize_1x128(xa)
+        tq = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_nt(a, sfa, b, sfb, None)
+        tg = time.perf_counter() - t0
+        t_full += tq + tg * (N / ns)
+        macs_sample += M * ns * K
+        total_bytes += gemm_bytes(M, N, K) + quant_bytes(M, K)
+    return {"value": total_bytes / t_full / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"all rows of each of the 6 decode GEMMs x the first {frac:.3f} of their columns "
+                       f"({macs_sample / 1e9:.2f} G multiply-adds of {full_macs / 1e9:.2f} G), plus the full "
+                       f"activation quantiser; time scaled to the whole step by the column fraction"),
+            "seconds_full_step_extrapolated": t_full}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "contiguous", "masked", "small"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dg.lib()
+
+    meta = {}
+    if args.workload == "decode":
+        jobs = dense_jobs(synth.DECODE)
+        bound = "hbm"
+    elif args.workload == "prefill":
+        jobs = dense_jobs(synth.PREFILL)
+        bound = "mfma"
+    elif args.workload == "small":
+        jobs = dense_jobs([synth.DENSE_SMALL])
+        bound = "hbm"
+    elif args.workload == "contiguous":
+        jobs, meta = contiguous_jobs()
+        bound = "mfma"
+    else:
+        jobs, meta = masked_jobs()
+        bound = "hbm"
+    log(f"workload {args.workload}: {[j.name for j in jobs]}, copies {[j.copies for j in jobs]}")
+
+    # step graphs: step s uses weight copy s of every job (period = max copies)
+    period = max(j.copies for j in jobs)
+    n_graphs = min(period, max(2, args.steps + args.warmup))
+    graphs = [capture(lambda s=s: [j.launch(s, True) for j in jobs]) for s in range(n_graphs)]
+    configs = []
+    for j in jobs:
+        j.launch(0, False)
+        configs.append(dg.last_config())
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % n_graphs].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % n_graphs].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    kms = kernel_durations(jobs)
+    step_bytes = sum(j.bytes_gemm + j.bytes_quant for j in jobs)
+    step_flops = sum(j.flops for j in jobs)
+    gemm_bytes_total = sum(j.bytes_gemm for j in jobs)
+    gemm_time_s = sum(kms) / 1e3
+    per_job = [{"name": j.name, "gemm_us": round(k * 1e3, 3),
+                "gemm_GBps": round(j.bytes_gemm / (k / 1e3) / 1e9, 1),
+                "gemm_TFLOPs": round(j.flops / (k / 1e3) / 1e12, 1), "config": cfg}
+               for j, k, cfg in zip(jobs, kms, configs)]
+
+    if bound == "hbm":
+        value = step_bytes / (ms_step / 1e3) / 1e9
+        unit = "GB/s"
+        achieved = gemm_bytes_total / gemm_time_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        value = step_flops / (ms_step / 1e3) / 1e12
+        unit = "TFLOP/s"
+        achieved = step_flops / gemm_time_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample")
+        cpu = cpu_baseline(args.workload, meta)
+
+    workload_desc = {
+        "decode": "decode-shaped dense FP8 NT GEMM, M in {64,128} x (N,K) in {(2112,7168),(24576,1536),(7168,16384)}, "
+                  "1x128/128x128 block scales, C=0, bf16 D",
+        "prefill": "prefill-shaped dense FP8 NT GEMM, M=4096 x (N,K) in {(4096,7168),(7168,2048),(24576,1536)}, "
+                   "C bf16, bf16 D",
+        "contiguous": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168",
+        "masked": "M-grouped masked FP8 GEMM, 16 experts x 256 rows, masked_m U[0,256], N=7168, K=2048",
+        "small": "dense FP8 NT GEMM M=128, N=256, K=512",
+    }[args.workload]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic: seeded N(0,1) fp32, quantised to e4m3 with 1x128 / 128x128 fp32 scales",
+        "config": {"workload": workload_desc, "step": "activation quantiser + GEMM per shape; weights pre-quantised",
+                   "graph_replay": True, **({"layout": meta} if meta else {})},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "frac_of_peak_step": round(value / (HBM_PEAK_GBS if bound == "hbm" else FP8_PEAK_TFLOPS), 4),
+        "per_gemm": per_job,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,11 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so
+// that register arrays are only ever indexed by constants (otherwise they
+// can be demoted to scratch memory).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 constexpr int kWave = 64;
 constexpr int kKBlock = 128;   // K width of one scale block and one MFMA
@@ -22,6 +35,17 @@ constexpr int kKBlock = 128;   // K width of one scale block and one MFMA
 // holds P[4*(l/16) + v][l % 16] in element v.
 __device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i &a, const v8i &b, const v4f &c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Promotion of a block partial: acc + p * s, element-wise, as whole-vector
+// values (element stores into an accumulator array would keep it in memory).
+__device__ __forceinline__ v4f promote(const v4f &acc, const v4f &p, const v4f &s) {
+    v4f r;
+    r.x = __builtin_fmaf(p.x, s.x, acc.x);
+    r.y = __builtin_fmaf(p.y, s.y, acc.y);
+    r.z = __builtin_fmaf(p.z, s.z, acc.z);
+    r.w = __builtin_fmaf(p.w, s.w, acc.w);
+    return r;
 }
 
 // fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet).

@@ -31,6 +31,11 @@ struct GemmProblem {
     int expected_m;   // masked only: host hint, <= 0 unknown
 };
 
+// Skinny-M family: dense with M <= 128, and the masked layout; needs K >= 256
+// and every operand below 2 GB (32-bit buffer offsets).
+bool skinny_eligible(const GemmProblem &p);
+hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
+
 // Chooses a kernel configuration, launches it on `stream`, and describes the
 // choice in `config`.  Returns the HIP error of the launch.
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);

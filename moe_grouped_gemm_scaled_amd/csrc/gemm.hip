@@ -148,28 +148,28 @@ gemm_tiled_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[LA], rb[LB];
-    float4 sa_cur[SM], sa_nxt[SM];
+    v4i ra[LA], rb[LB];
+    v4f sa_cur[SM], sa_nxt[SM];
     float sb_cur, sb_nxt = 0.f;
 
-    auto load_tiles = [&](int kb) {
+    auto load_tiles = [&](int kb) __attribute__((always_inline)) {
         const int64_t koff = (int64_t)kb * kKBlock;
 #pragma unroll
-        for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const uint4 *>(ga[i] + koff);
+        for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const v4i *>(ga[i] + koff);
 #pragma unroll
-        for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const uint4 *>(gb[i] + koff);
+        for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const v4i *>(gb[i] + koff);
     };
-    auto store_tiles = [&](int stage) {
+    auto store_tiles = [&](int stage) __attribute__((always_inline)) {
         uint8_t *base = lds + stage * STAGE;
 #pragma unroll
-        for (int i = 0; i < LA; ++i) *reinterpret_cast<uint4 *>(base + la_off[i]) = ra[i];
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<v4i *>(base + la_off[i]) = ra[i];
 #pragma unroll
-        for (int i = 0; i < LB; ++i) *reinterpret_cast<uint4 *>(base + lb_off[i]) = rb[i];
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<v4i *>(base + lb_off[i]) = rb[i];
     };
-    auto load_scales = [&](int kb, float4 *sa, float &sb) {
+    auto load_scales = [&](int kb, v4f *sa, float &sb) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < SM; ++i)
-            sa[i] = *reinterpret_cast<const float4 *>(SFA + (int64_t)kb * ld + sa_row[i]);
+            sa[i] = *reinterpret_cast<const v4f *>(SFA + (int64_t)kb * ld + sa_row[i]);
         sb = SFB[nb * nkb + kb];
     };
 
@@ -193,26 +193,23 @@ gemm_tiled_kernel(GemmParams p) {
         for (int j = 0; j < SN; ++j) {
             const int row = wn0 + 16 * j + l16;
             const uint8_t *rp = sB + row * kKBlock;
-            const uint4 lo = *reinterpret_cast<const uint4 *>(rp + ((g4 ^ (row & 7)) << 4));
-            const uint4 hi = *reinterpret_cast<const uint4 *>(rp + (((g4 + 4) ^ (row & 7)) << 4));
+            const v4i lo = *reinterpret_cast<const v4i *>(rp + ((g4 ^ (row & 7)) << 4));
+            const v4i hi = *reinterpret_cast<const v4i *>(rp + (((g4 + 4) ^ (row & 7)) << 4));
             bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
             const int row = wm0 + 16 * i + l16;
             const uint8_t *rp = sA + row * kKBlock;
-            const uint4 lo = *reinterpret_cast<const uint4 *>(rp + ((g4 ^ (row & 7)) << 4));
-            const uint4 hi = *reinterpret_cast<const uint4 *>(rp + (((g4 + 4) ^ (row & 7)) << 4));
+            const v4i lo = *reinterpret_cast<const v4i *>(rp + ((g4 ^ (row & 7)) << 4));
+            const v4i hi = *reinterpret_cast<const v4i *>(rp + (((g4 + 4) ^ (row & 7)) << 4));
             const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            const float s0 = sa_cur[i].x * sb_cur, s1 = sa_cur[i].y * sb_cur;
-            const float s2 = sa_cur[i].z * sb_cur, s3 = sa_cur[i].w * sb_cur;
+            const v4f sv = v4f{sa_cur[i].x * sb_cur, sa_cur[i].y * sb_cur, sa_cur[i].z * sb_cur,
+                               sa_cur[i].w * sb_cur};
 #pragma unroll
             for (int j = 0; j < SN; ++j) {
                 const v4f pp = mfma_16x16x128_e4m3(af, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
-                acc[i][j].x = __builtin_fmaf(pp.x, s0, acc[i][j].x);
-                acc[i][j].y = __builtin_fmaf(pp.y, s1, acc[i][j].y);
-                acc[i][j].z = __builtin_fmaf(pp.z, s2, acc[i][j].z);
-                acc[i][j].w = __builtin_fmaf(pp.w, s3, acc[i][j].w);
+                acc[i][j] = promote(acc[i][j], pp, sv);
             }
         }
         if (more) {
@@ -274,13 +271,14 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
 }
 
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
-    (void)num_cus;
     switch (p.mode) {
     case Mode::Dense:
+        if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
         return launch_tiled<128, 128, 2, 2, Mode::Dense>(p, stream, config);
     case Mode::Contig:
         return launch_tiled<128, 128, 2, 2, Mode::Contig>(p, stream, config);
     case Mode::Masked:
+        if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
         return launch_tiled<128, 128, 2, 2, Mode::Masked>(p, stream, config);
     }
     return hipErrorInvalidValue;
