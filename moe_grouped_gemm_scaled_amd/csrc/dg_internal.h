@@ -36,6 +36,11 @@ struct GemmProblem {
 bool skinny_eligible(const GemmProblem &p);
 hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
 
+// Large-tile family (prefill-shaped dense, contiguous grouped); needs every
+// operand below 2 GB (32-bit buffer offsets).
+bool wide_eligible(const GemmProblem &p);
+hipError_t launch_wide(const GemmProblem &p, hipStream_t stream, std::string &config);
+
 // Chooses a kernel configuration, launches it on `stream`, and describes the
 // choice in `config`.  Returns the HIP error of the launch.
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);

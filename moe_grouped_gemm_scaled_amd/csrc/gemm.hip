@@ -274,8 +274,10 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
     switch (p.mode) {
     case Mode::Dense:
         if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
+        if (wide_eligible(p)) return launch_wide(p, stream, config);
         return launch_tiled<128, 128, 2, 2, Mode::Dense>(p, stream, config);
     case Mode::Contig:
+        if (wide_eligible(p)) return launch_wide(p, stream, config);
         return launch_tiled<128, 128, 2, 2, Mode::Contig>(p, stream, config);
     case Mode::Masked:
         if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
