@@ -19,6 +19,8 @@
 // grouped layout (expert looked up from the first row of the tile) and the
 // masked grouped layout (tiles at or beyond masked_m[g] exit at once).
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "dg_device.h"
 #include "dg_internal.h"
@@ -270,7 +272,31 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
     return hipGetLastError();
 }
 
+// Kernel family override for tuning: DG_KERNEL_FAMILY=skinny|wide|tiled picks
+// that family wherever it supports the problem (read once per process).
+static int family_override() {
+    static const int f = [] {
+        const char *e = getenv("DG_KERNEL_FAMILY");
+        if (!e) return 0;
+        if (!strcmp(e, "skinny")) return 1;
+        if (!strcmp(e, "wide")) return 2;
+        if (!strcmp(e, "tiled")) return 3;
+        return 0;
+    }();
+    return f;
+}
+
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
+    const int f = family_override();
+    if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
+    if (f == 2 && wide_eligible(p)) return launch_wide(p, stream, config);
+    if (f == 3) {
+        switch (p.mode) {
+        case Mode::Dense: return launch_tiled<128, 128, 2, 2, Mode::Dense>(p, stream, config);
+        case Mode::Contig: return launch_tiled<128, 128, 2, 2, Mode::Contig>(p, stream, config);
+        case Mode::Masked: return launch_tiled<128, 128, 2, 2, Mode::Masked>(p, stream, config);
+        }
+    }
     switch (p.mode) {
     case Mode::Dense:
         if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
