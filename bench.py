@@ -182,15 +182,24 @@ def masked_jobs():
 # timing
 # ---------------------------------------------------------------------------
 
+_CAPTURE_STREAM = None
+
+
 def capture(fn):
+    """Capture fn() into a graph on one dedicated stream, after an eager call on
+    that same stream: the library's per-(device, stream) split-K workspace is
+    allocated by the eager call and reused by the captured launches (a stream
+    seen for the first time under capture would fall back to no split)."""
+    global _CAPTURE_STREAM
+    if _CAPTURE_STREAM is None:
+        _CAPTURE_STREAM = torch.cuda.Stream()
+    s = _CAPTURE_STREAM
     g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         fn()                         # warm: first-call allocations happen outside capture
-    torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):
         fn()
     torch.cuda.synchronize()
     return g
@@ -277,6 +286,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "contiguous", "masked", "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 20 device-to-device copies of MIB MiB each (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -285,6 +296,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 20}), flush=True)
+        return
     dg.lib()
 
     meta = {}
@@ -310,9 +330,10 @@ def main():
     n_graphs = min(period, max(2, args.steps + args.warmup))
     graphs = [capture(lambda s=s: [j.launch(s, True) for j in jobs]) for s in range(n_graphs)]
     configs = []
-    for j in jobs:
-        j.launch(0, False)
-        configs.append(dg.last_config())
+    with torch.cuda.stream(_CAPTURE_STREAM):       # the stream the graphs were captured on
+        for j in jobs:
+            j.launch(0, False)
+            configs.append(dg.last_config())
     torch.cuda.synchronize()
 
     for i in range(args.warmup):

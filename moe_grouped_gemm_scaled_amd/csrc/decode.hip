@@ -404,7 +404,7 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 // Returns false when no large-enough workspace exists and none may be
 // allocated now (the stream is being captured into a graph).
-static bool get_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters, float **ws, int **counters) {
+bool get_splitk_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters, float **ws, int **counters) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -466,7 +466,7 @@ static hipError_t launch_skinny_t(const GemmProblem &p, int splits, hipStream_t 
     if (splits > 1) {
         const size_t per = (size_t)ROWS * BN * sizeof(float);
         if ((int64_t)splits * ROWS * BN * 4 >= ((int64_t)1 << 31) ||
-            !get_workspace(stream, per * tiles * splits, (size_t)tiles, &k.ws, &k.counters))
+            !get_splitk_workspace(stream, per * tiles * splits, (size_t)tiles, &k.ws, &k.counters))
             splits = 1;
     }
     k.splits = splits;

@@ -36,10 +36,17 @@ struct GemmProblem {
 bool skinny_eligible(const GemmProblem &p);
 hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
 
-// Large-tile family (prefill-shaped dense, contiguous grouped); needs every
-// operand below 2 GB (32-bit buffer offsets).
-bool wide_eligible(const GemmProblem &p);
-hipError_t launch_wide(const GemmProblem &p, hipStream_t stream, std::string &config);
+// Pipelined family (multi-stage LDS-DMA pipeline, optional split-K): every
+// mode and shape; needs every operand below 2 GB (32-bit buffer offsets).
+bool pipe_eligible(const GemmProblem &p);
+hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
+
+// Split-K workspace of the calling device for `stream`: at least `ws_bytes`
+// of fp32 partials and `n_counters` zeroed arrival counters, grown on demand
+// (completed calls leave the counters zeroed).  Returns false when none large
+// enough exists and none may be allocated now (the stream is being captured
+// into a graph); the caller then runs without split-K.
+bool get_splitk_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters, float **ws, int **counters);
 
 // Chooses a kernel configuration, launches it on `stream`, and describes the
 // choice in `config`.  Returns the HIP error of the launch.

@@ -272,14 +272,14 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
     return hipGetLastError();
 }
 
-// Kernel family override for tuning: DG_KERNEL_FAMILY=skinny|wide|tiled picks
+// Kernel family override for tuning: DG_KERNEL_FAMILY=skinny|pipe|tiled picks
 // that family wherever it supports the problem (read once per process).
 static int family_override() {
     static const int f = [] {
         const char *e = getenv("DG_KERNEL_FAMILY");
         if (!e) return 0;
         if (!strcmp(e, "skinny")) return 1;
-        if (!strcmp(e, "wide")) return 2;
+        if (!strcmp(e, "pipe")) return 2;
         if (!strcmp(e, "tiled")) return 3;
         return 0;
     }();
@@ -289,7 +289,7 @@ static int family_override() {
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     const int f = family_override();
     if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
-    if (f == 2 && wide_eligible(p)) return launch_wide(p, stream, config);
+    if (f == 2 && pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);
     if (f == 3) {
         switch (p.mode) {
         case Mode::Dense: return launch_tiled<128, 128, 2, 2, Mode::Dense>(p, stream, config);
@@ -297,13 +297,18 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
         case Mode::Masked: return launch_tiled<128, 128, 2, 2, Mode::Masked>(p, stream, config);
         }
     }
+    // Decode-shaped dense problems with enough 128-column tiles to occupy
+    // most CUs without splitting K run faster on the skinny family (no split
+    // partials; measured for M in {64, 128}, N = 24576, K = 1536).
+    const int cus = num_cus > 0 ? num_cus : 256;
+    if (p.mode == Mode::Dense && p.rows_a <= 128 && skinny_eligible(p) && (int64_t)(p.N + 127) / 128 * 10 >= (int64_t)cus * 7)
+        return launch_skinny(p, num_cus, stream, config);
+    if (pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);
     switch (p.mode) {
     case Mode::Dense:
         if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
-        if (wide_eligible(p)) return launch_wide(p, stream, config);
         return launch_tiled<128, 128, 2, 2, Mode::Dense>(p, stream, config);
     case Mode::Contig:
-        if (wide_eligible(p)) return launch_wide(p, stream, config);
         return launch_tiled<128, 128, 2, 2, Mode::Contig>(p, stream, config);
     case Mode::Masked:
         if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);

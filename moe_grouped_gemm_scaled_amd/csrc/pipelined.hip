@@ -1,0 +1,678 @@
+// pipelined.hip -- FP8 block-scaled NT GEMM for gfx950 with a multi-stage
+// LDS pipeline filled by DMA: one kernel template for decode shapes (few
+// rows, long K, optional split-K), prefill shapes and the M-grouped
+// contiguous and masked layouts.
+//
+// Arithmetic (per 128-wide K block: one v_mfma_f32_16x16x128_f8f6f4 partial
+// per 16x16 subtile, promoted into the fp32 accumulator with
+// sfa[kb][m] * sfb[n/128][kb]) follows the two-level accumulation of
+// "DeepSeek open-sources DeepGEMM", picoinsstore, applied to the FP8 GEMM
+// interface of the "DeepGEMM" README summary, GeekNews.  Organisation:
+//  - a workgroup of WGM x WGN waves owns a BM x BN tile of one group (and,
+//    with split-K, one range of its K blocks); each wave owns a
+//    (BM/WGM) x (BN/WGN) sub-tile, so every byte read from LDS feeds several
+//    MFMAs;
+//  - K blocks stream through NST LDS stages filled by buffer loads that write
+//    LDS directly (no staging registers), NST-1 blocks ahead.  Every wave
+//    issues the same number of such loads per block, so waiting for all but
+//    the newest NST-2 blocks is one s_waitcnt with a constant count, and the
+//    barrier between blocks waits for LDS reads only.  The stored layout
+//    XOR-swizzles 16-byte chunks by row, so fragment reads of 16 consecutive
+//    rows spread over the banks.  Within a K block a wave software-pipelines
+//    its row subtiles: the A fragment of the next subtile is read (and, with
+//    DEEP, the previous subtile promoted) while the MFMAs of the current one
+//    run;
+//  - split-K: S workgroups cover disjoint K ranges of one tile.  Each writes
+//    its fp32 partial with device-coherent (sc1) 16-byte stores, waits for
+//    them and bumps a per-tile counter; the last to arrive reads the partials
+//    the same way, sums them in split order (the same result whatever the
+//    arrival order), finishes the tile and resets the counter.  All
+//    cross-workgroup data moves through device-coherent accesses, so no L2
+//    writeback or invalidate is needed;
+//  - the epilogue loads all of C under a wave's tile at once, then stages the
+//    fp32 tile through LDS in 32-row chunks so that D is written as 16-byte
+//    row segments.
+// Without split-K, workgroups are numbered so that consecutive tiles of one
+// group run on the same XCD (shared L2) in a grouped raster.
+#include <stdio.h>
+
+#include <atomic>
+
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+
+struct PipeParams {
+    const uint8_t *a;
+    const float *sfa;
+    const uint8_t *b;
+    const float *sfb;
+    const uint16_t *c;
+    uint16_t *d;
+    const int32_t *idx;        // m_indices (contiguous) or masked_m (masked)
+    float *ws;                 // split-K partials (splits > 1)
+    int *counters;             // split-K arrival counters, one per tile (splits > 1)
+    int rows_a, N, K, ld_sfa, G;
+    int tiles_m, tiles_n, gm;
+    // split-K: tiles [0, split_hi) have splits_lo + 1 splits, the others
+    // splits_lo; `slots` = partial slots per tile in `ws`
+    int splits_lo, split_hi, slots;
+};
+
+#define DG_LDS(ptr) ((__attribute__((address_space(3))) void *)(ptr))
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone, n < 64
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
+
+// Workgroup barrier for LDS stages filled by DMA: waits for this wave's LDS
+// reads (lgkmcnt(0)) but not for its loads in flight, which the caller has
+// waited for with an explicit count.  The wavefront-scope fences keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// DMA of one pipeline step (KS K blocks) into an LDS stage: DA (DB) 1-KB
+// chunks of A (B) per wave, chunk i landing at lds_a + i*STEP_A (lds_b +
+// i*STEP_B), then one 1-KB load of scales, so that every wave issues
+// DA + DB + 1 loads per step.  A device-only function: the host compilation
+// pass does not accept the LDS address-space cast inside the kernel's lambdas.
+template <int DA, int DB, int STEP_A, int STEP_B>
+__device__ __forceinline__ void dma_step(uint8_t *stg, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
+                                         __amdgpu_buffer_rsrc_t rS, const int *va, const int *vb, int v_s, int lds_a,
+                                         int lds_b, int lds_s, int k_off, int s_off) {
+#pragma unroll
+    for (int i = 0; i < DA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, DG_LDS(stg + lds_a + i * STEP_A), 16, va[i], k_off, 0, 0);
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, DG_LDS(stg + lds_b + i * STEP_B), 16, vb[i], k_off, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, DG_LDS(stg + lds_s), 16, v_s, s_off, 0, 0);
+}
+
+// An integer the optimiser cannot see through (an empty asm statement that
+// "changes" it), used for LDS offsets so that address arithmetic is not
+// shared between reads.
+__device__ __forceinline__ int opaque_offset(int x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
+// Steps U, U+1, .. of one round of the K loop, step U + i running only when
+// b + U + i < n.  Nested (not sequential) conditions: the control flow then
+// has no path that skips a step and runs a later one, so the compiler's count
+// of loads in flight stays exact and it adds no waits of its own.
+template <int U, int NST, class F>
+__device__ __forceinline__ void nested_steps(int b, int n, F &&f) {
+    if constexpr (U < NST) {
+        if (b + U < n) {                           // uniform
+            f(std::integral_constant<int, U>{});
+            nested_steps<U + 1, NST>(b, n, f);
+        }
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+pipe_kernel(PipeParams p) {
+    constexpr int NW = WGM * WGN;
+    constexpr int TM = BM / WGM, TN = BN / WGN;   // wave tile
+    constexpr int SM = TM / 16, SN = TN / 16;     // MFMA subtiles per wave
+    constexpr int NBW = BN >= 128 ? BN / 128 : 1; // 128-wide scale blocks under the tile's columns
+    // stage layout: KS K blocks of A (BM x 128 B each), KS of B, then per K
+    // block kk a 1-KB slot of A scales (sfa[kb+kk][m0 + 4l .. +3] at 16 l),
+    // then 1 KB of B scales (sfb[n0/128 + l][kb .. kb+3] at 16 l)
+    constexpr int BLK_A = BM * kKBlock, BLK_B = BN * kKBlock;
+    constexpr int OFF_B = KS * BLK_A;
+    constexpr int OFF_SA = OFF_B + KS * BLK_B;
+    constexpr int OFF_SB = OFF_SA + KS * 1024;
+    constexpr int STAGE = OFF_SB + 1024;
+    constexpr int DA = KS * BM / (8 * NW), DB = KS * BN / (8 * NW);   // 1-KB LDS-DMA chunks per wave per step
+    constexpr int PER_BLOCK = DA + DB + 1;        // loads per wave per step
+    static_assert(KS == 1 || KS == 2 || KS == 4, "K blocks per stage");
+    static_assert(NW % KS == 0 && NW > KS, "waves [0, KS) fetch A scales, the others B scales");
+    constexpr int EPI_ROWS = 32;                  // epilogue chunk rows per wave
+    constexpr int EPI_PITCH = TN + 4;             // floats per staged row (padding spreads banks)
+    static_assert(NST >= 2 && NST <= 6 && NST * STAGE <= 160 * 1024, "stages fit the LDS");
+    static_assert(DA >= 1 && DB >= 1 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "DMA chunks split evenly");
+    static_assert((NST - 2) * PER_BLOCK < 64, "vmcnt immediate");
+    static_assert(BM / 4 <= 64 && NBW <= 64, "one scale DMA per wave per K block");
+    static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns share one scale block");
+    static_assert(TM % EPI_ROWS == 0 && (TN % 8) == 0, "epilogue chunks");
+    static_assert(NW % 2 == 0 && (NW / 2) * EPI_ROWS * EPI_PITCH * 4 <= STAGE,
+                  "epilogue staging: half the waves per stage");
+
+    // the stages are separate objects, so that the compiler can tell reads of
+    // one from DMA into another
+    __shared__ __attribute__((aligned(16))) uint8_t stage0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t stage1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t stage2[NST > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage3[NST > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage4[NST > 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage5[NST > 5 ? STAGE : 16];
+    auto stage_of = [&](auto sc) __attribute__((always_inline)) -> uint8_t * {
+        constexpr int s = decltype(sc)::value;
+        if constexpr (s == 0) return stage0;
+        else if constexpr (s == 1) return stage1;
+        else if constexpr (s == 2) return stage2;
+        else if constexpr (s == 3) return stage3;
+        else if constexpr (s == 4) return stage4;
+        else return stage5;
+    };
+
+    const int K = p.K, N = p.N;
+    const int nkb = K / kKBlock;
+    const int nnb = (N + 127) / 128;
+    const int tiles_per_group = p.tiles_m * p.tiles_n;
+    const int total = tiles_per_group * (MODE == Mode::Masked ? p.G : 1);
+
+    // ---- work unit: tile t_all (group, m-tile, n-tile) and, with split-K,
+    // split s of S (the splits of a tile are adjacent workgroups; the first
+    // split_hi tiles have one split more than the others)
+    int t_all = 0, s = 0, S = 1;
+    if (SPLIT) {
+        const int id = blockIdx.x;
+        const int first = p.split_hi * (p.splits_lo + 1);
+        if (id < first) {
+            S = p.splits_lo + 1;
+            t_all = id / S;
+            s = id % S;
+        } else {
+            S = p.splits_lo;
+            t_all = p.split_hi + (id - first) / S;
+            s = (id - first) % S;
+        }
+    } else {
+        t_all = xcd_remap(blockIdx.x, total);
+    }
+    int t_lin = t_all;
+    int grp = 0;
+    if (MODE == Mode::Masked) {
+        grp = t_lin / tiles_per_group;
+        t_lin -= grp * tiles_per_group;
+    }
+    int tm, tn;
+    if (SPLIT) {
+        tm = t_lin / p.tiles_n;
+        tn = t_lin % p.tiles_n;
+    } else {
+        raster(t_lin, p.tiles_m, p.tiles_n, p.gm, tm, tn);
+    }
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    // K range of this workgroup, in steps of KS blocks (nkb is a multiple of KS)
+    const int nsteps_all = nkb / KS;
+    const int st0 = SPLIT ? (int)((int64_t)nsteps_all * s / S) : 0;
+    const int st1 = SPLIT ? (int)((int64_t)nsteps_all * (s + 1) / S) : nsteps_all;
+    const int nblk = st1 - st0;                    // steps
+
+    const uint8_t *A = p.a;
+    const float *SFA = p.sfa;
+    const uint8_t *B = p.b;
+    const float *SFB = p.sfb;
+    const uint16_t *C = p.c;
+    uint16_t *D = p.d;
+    const int rows_a = p.rows_a;
+    const int ld = p.ld_sfa;
+    int valid_m = rows_a;
+    if (MODE == Mode::Masked) {
+        int mm = p.idx[grp];
+        mm = mm < 0 ? 0 : (mm > rows_a ? rows_a : mm);
+        if (m0 >= mm) return;                      // uniform exit, before any barrier
+        valid_m = mm;
+        A += (int64_t)grp * rows_a * K;
+        SFA += (int64_t)grp * nkb * ld;
+        B += (int64_t)grp * N * K;
+        SFB += (int64_t)grp * nnb * nkb;
+        if (C) C += (int64_t)grp * rows_a * N;
+        D += (int64_t)grp * rows_a * N;
+    } else if (MODE == Mode::Contig) {
+        const int e = p.idx[m0];
+        if (e < 0) return;                         // tile of padding rows: uniform exit
+        B += (int64_t)e * N * K;
+        SFB += (int64_t)e * nnb * nkb;
+    }
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int l16 = lane & 15;
+    const int g4 = lane >> 4;
+
+    // ---- DMA plan.  A step's A tile is KS*BM/8 1-KB chunks: chunk c holds
+    // rows 8(c / KS) .. +7 of K block c % KS.  Wave w issues chunks
+    // c = w + NW*i, so its K block w % KS is fixed and its rows advance by
+    // 8*NW/KS per instruction (likewise for B).  Lane l lands at row +l/8,
+    // 16-byte chunk l%8, so it fetches global chunk (l%8) ^ (row & 7) =
+    // (l%8) ^ (l/8) of that row: the stored layout XOR-swizzles 16-byte chunks
+    // by (row & 7).  Rows past the matrix clamp to its last row (their
+    // products are never stored).
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, N * K, 0x00020000);
+    const int dchunk = ((lane & 7) ^ (lane >> 3)) * 16;
+    const int wk = wave % KS, wr = wave / KS;      // K block and first row group of this wave's chunks
+    constexpr int RG_STEP = NW / KS;               // row groups between a wave's chunks
+    int va[DA], vb[DB];
+    static_for<DA>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        va[i] = min(m0 + 8 * (wr + RG_STEP * i) + (lane >> 3), rows_a - 1) * K + wk * kKBlock + dchunk;
+    });
+    static_for<DB>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        vb[i] = min(n0 + 8 * (wr + RG_STEP * i) + (lane >> 3), N - 1) * K + wk * kKBlock + dchunk;
+    });
+    const int lds_a = wk * BLK_A + wr * 1024;
+    const int lds_b = OFF_B + wk * BLK_B + wr * 1024;
+    // scales: lane l of wave w < KS fetches sfa[kb + w][m0 + 4l .. +3] (16 B);
+    // lane l of every other wave the 16 B starting at sfb[n0/128 + l][kb]
+    // (the scales of K blocks kb .. kb+3; all of these waves write the same
+    // bytes).  Lanes past the tile fetch harmless in-range or zero-filled data
+    // into unused slots.
+    const bool wsa = wave < KS;
+    const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+        wsa ? (void *)SFA : (void *)SFB, (short)0, wsa ? nkb * ld * 4 : nnb * nkb * 4, 0x00020000);
+    const int sa_row = m0 + 4 * lane;
+    const int v_s = wsa ? ((sa_row < ld ? sa_row : 0) + wave * ld) * 4 : min(n0 / 128 + lane, nnb - 1) * nkb * 4;
+    const int lds_s = wsa ? OFF_SA + wave * 1024 : OFF_SB;
+    const int s_stride = wsa ? ld * 4 : 4;
+
+    // DMA of step st (K blocks KS*st .. +KS-1) into stage stg
+    auto dma = [&](uint8_t *stg, int st) __attribute__((always_inline)) {
+        const int kb = st * KS;
+        dma_step<DA, DB, RG_STEP * 1024, RG_STEP * 1024>(stg, rA, rB, rS, va, vb, v_s, lds_a, lds_b, lds_s,
+                                                         kb * kKBlock, kb * s_stride);
+    };
+
+    v4f acc[SM][SN];
+    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+            acc[decltype(ic)::value][decltype(jc)::value] = v4f{0.f, 0.f, 0.f, 0.f};
+        });
+    });
+    const int wave_nb = ((wn * TN) / 128) < NBW ? (wn * TN) / 128 : 0;
+
+    // Byte offsets within a stage of the fragments this lane reads: the two
+    // 16-byte halves of B subtile j and A subtile i, and the A scales of
+    // subtile i.  Each is made opaque to the optimiser, so that every LDS read
+    // is one address computation from its stage object: the compiler can then
+    // tell which stage a read touches and adds no waits for DMA into other
+    // stages.
+    int off_b[SN][2], off_a[SM][2], off_sa[SM];
+    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        const int row = (wn * SN + j) * 16 + l16;
+        off_b[j][0] = opaque_offset(OFF_B + row * kKBlock + ((g4 ^ (row & 7)) << 4));
+        off_b[j][1] = opaque_offset(OFF_B + row * kKBlock + (((g4 + 4) ^ (row & 7)) << 4));
+    });
+    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        const int row = (wm * SM + i) * 16 + l16;
+        off_a[i][0] = opaque_offset(row * kKBlock + ((g4 ^ (row & 7)) << 4));
+        off_a[i][1] = opaque_offset(row * kKBlock + (((g4 + 4) ^ (row & 7)) << 4));
+        off_sa[i] = opaque_offset(OFF_SA + ((wm * SM + i) * 16 + 4 * g4) * 4);
+    });
+    const int off_sb = OFF_SB + 16 * wave_nb;
+
+    // Multiply K block kk of the step held in `stg`.  Software pipeline over
+    // the wave's row subtiles: the A fragment of subtile i+1 is read while the
+    // MFMAs of subtile i run; with DEEP, subtile i-1 is also promoted then.
+    auto compute_block = [&](const uint8_t *stg_step, auto kkc) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kkc)::value;
+        const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
+        const uint8_t *stg = stg_step + kk * BLK_A;        // A block kk; B block kk is at stg_b
+        const uint8_t *stg_b = stg_step + kk * BLK_B;
+        const uint8_t *stg_s = stg_step + kk * 1024;       // A scales of block kk
+        v8i bf[SN];
+        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b[j][0]);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b[j][1]);
+            bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        });
+        auto read_a = [&](auto ic, v8i &af, v4f &sa) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a[i][0]);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a[i][1]);
+            af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            sa = *reinterpret_cast<const v4f *>(stg_s + off_sa[i]);
+        };
+        v8i af_cur, af_nxt;
+        v4f sa_cur, sa_nxt;
+        read_a(std::integral_constant<int, 0>{}, af_cur, sa_cur);
+        if constexpr (DEEP) {
+            // promote subtile i-1 while the MFMAs of subtile i run (two sets of partials live)
+            v4f sa_prv;
+            v4f pp_prv[SN];
+            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i + 1 < SM) read_a(std::integral_constant<int, i + 1>{}, af_nxt, sa_nxt);
+                v4f pp[SN];
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    pp[j] = mfma_16x16x128_e4m3(af_cur, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+                });
+                if constexpr (i > 0) {
+                    const v4f sv = v4f{sa_prv.x * sb, sa_prv.y * sb, sa_prv.z * sb, sa_prv.w * sb};
+                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                        constexpr int j = decltype(jc)::value;
+                        acc[i - 1][j] = promote(acc[i - 1][j], pp_prv[j], sv);
+                    });
+                }
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    pp_prv[decltype(jc)::value] = pp[decltype(jc)::value];
+                });
+                sa_prv = sa_cur;
+                if constexpr (i + 1 < SM) {
+                    af_cur = af_nxt;
+                    sa_cur = sa_nxt;
+                }
+            });
+            const v4f sv = v4f{sa_prv.x * sb, sa_prv.y * sb, sa_prv.z * sb, sa_prv.w * sb};
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                acc[SM - 1][j] = promote(acc[SM - 1][j], pp_prv[j], sv);
+            });
+        } else {
+            // promote each subtile right after its MFMAs (the other wave on the
+            // SIMD covers the MFMA latency)
+            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i + 1 < SM) read_a(std::integral_constant<int, i + 1>{}, af_nxt, sa_nxt);
+                v4f pp[SN];
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    pp[j] = mfma_16x16x128_e4m3(af_cur, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+                });
+                const v4f sv = v4f{sa_cur.x * sb, sa_cur.y * sb, sa_cur.z * sb, sa_cur.w * sb};
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    acc[i][j] = promote(acc[i][j], pp[j], sv);
+                });
+                if constexpr (i + 1 < SM) {
+                    af_cur = af_nxt;
+                    sa_cur = sa_nxt;
+                }
+            });
+        }
+    };
+
+    auto compute = [&](const uint8_t *stg) __attribute__((always_inline)) {
+        static_for<KS>([&](auto kkc) __attribute__((always_inline)) { compute_block(stg, kkc); });
+    };
+
+    // ---- K loop over NST stages: local step j (global step st0 + j) lives in
+    // stage (j + NST - 1) mod NST.  Step j waits for its data (the next NST-2
+    // steps stay in flight), meets the other waves at the barrier (after which
+    // the stage read in the previous step is free), refills that stage with
+    // step j + NST - 1 and multiplies step j.  The loop starts NST-1 steps
+    // early, so that the first DMAs are issued by the same instructions as the
+    // others; indices past the end re-fetch the last step, which is then never
+    // multiplied.
+    constexpr int kWaitPipe = wait_vmcnt((NST - 2) * PER_BLOCK);
+#pragma clang loop unroll(disable)   // no peeled first round: one copy of every DMA keeps the wait counts exact
+    for (int b = -(NST - 1); b < nblk; b += NST) {
+        nested_steps<0, NST>(b, nblk, [&](auto sc) __attribute__((always_inline)) {
+            constexpr int u = decltype(sc)::value;
+            const int j = b + u;
+            __builtin_amdgcn_s_waitcnt(kWaitPipe);
+            lds_barrier();
+            dma(stage_of(sc), st0 + min(j + NST - 1, nblk - 1));
+            if (j >= 0) compute(stage_of(std::integral_constant<int, (u + 1) % NST>{}));
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    lds_barrier();
+
+    // ---- split-K: every split publishes its partial; the last to arrive sums
+    // all of them in split order and finishes the tile
+    if constexpr (SPLIT) {
+        if (S > 1) {
+            __shared__ int is_last;
+            constexpr int PART = BM * BN;                    // floats per (tile, split)
+            constexpr int CPOL_COHERENT = 16;                // sc1
+            const __amdgpu_buffer_rsrc_t rW =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(p.ws + (int64_t)t_all * p.slots * PART), (short)0,
+                                                  S * PART * 4, 0x00020000);
+            const int base = (wave * (SM * SN * 64) + lane) * 16;   // bytes, fragment order
+            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), rW,
+                                                           base + (i * SN + j) * 64 * 16, s * PART * 4,
+                                                           CPOL_COHERENT);
+                });
+            });
+            __builtin_amdgcn_s_waitcnt(0);                  // partial stores complete before the count
+            __syncthreads();
+            if (tid == 0)
+                is_last = __hip_atomic_fetch_add(p.counters + t_all, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+            __syncthreads();
+            if (!is_last) return;
+            v4f sum[SM][SN];
+            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    sum[decltype(ic)::value][decltype(jc)::value] = v4f{0.f, 0.f, 0.f, 0.f};
+                });
+            });
+            for (int s2 = 0; s2 < S; ++s2) {
+                v4f part[SM][SN];
+                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                    constexpr int i = decltype(ic)::value;
+                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                        constexpr int j = decltype(jc)::value;
+                        part[i][j] = __builtin_bit_cast(
+                            v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, base + (i * SN + j) * 64 * 16,
+                                                                       s2 * PART * 4, CPOL_COHERENT));
+                    });
+                });
+                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                    constexpr int i = decltype(ic)::value;
+                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                        constexpr int j = decltype(jc)::value;
+                        sum[i][j] += s2 == s ? acc[i][j] : part[i][j];
+                    });
+                });
+            }
+            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    acc[decltype(ic)::value][decltype(jc)::value] = sum[decltype(ic)::value][decltype(jc)::value];
+                });
+            });
+            if (tid == 0) __hip_atomic_store(p.counters + t_all, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // ---- epilogue.  Each wave first loads all of C under its tile (one
+    // 16-byte load per 8 columns, all in flight together), then stages 32 fp32
+    // rows at a time in LDS and reads them back as 8 consecutive columns per
+    // lane, to add C and write D with 16-byte stores (scalar accesses when N
+    // is not a multiple of 8).
+    float *stage = reinterpret_cast<float *>(wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * (EPI_ROWS * EPI_PITCH);
+    const int row0 = m0 + wm * TM;
+    const int col0 = n0 + wn * TN;
+    constexpr int SEG = TN / 8;                  // 8-column segments per row
+    constexpr int NQ = EPI_ROWS * SEG / 64;      // items per lane per chunk
+    constexpr int NCH = TM / EPI_ROWS;
+    static_assert(TM <= 64 && (EPI_ROWS * SEG) % 64 == 0, "row mask and item split");
+    // rows of the wave's tile that are stored, one bit each
+    uint64_t rows_ok;
+    {
+        const int r = row0 + lane;
+        bool ok = lane < TM && r < valid_m;
+        if (MODE == Mode::Contig) ok = ok && p.idx[r] >= 0;
+        rows_ok = __ballot(ok);
+    }
+    const bool vec = (N % 8) == 0;
+    v4i cr[NCH][NQ];
+    static_for<NCH>([&](auto cc) __attribute__((always_inline)) {
+        static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int c = decltype(cc)::value, q = decltype(qc)::value;
+            const int item = q * 64 + lane;
+            const int r = c * EPI_ROWS + item / SEG;
+            const int col = col0 + (item % SEG) * 8;
+            cr[c][q] = v4i{0, 0, 0, 0};
+            if (C && vec && ((rows_ok >> r) & 1) && col < N)
+                cr[c][q] = *reinterpret_cast<const v4i *>(C + (int64_t)(row0 + r) * N + col);
+        });
+    });
+    static_for<NCH>([&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value;
+        static_for<EPI_ROWS / 16>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int ii = decltype(ic)::value;
+            constexpr int i = c * (EPI_ROWS / 16) + ii;
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                const v4f a4 = acc[i][j];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) stage[(ii * 16 + 4 * g4 + v) * EPI_PITCH + j * 16 + l16] = a4[v];
+            });
+        });
+        static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            const int item = q * 64 + lane;
+            const int rl = item / SEG, sgi = item % SEG;
+            const int r = c * EPI_ROWS + rl;
+            const int row = row0 + r;
+            const int col = col0 + sgi * 8;
+            if (((rows_ok >> r) & 1) && col < N) {
+                const float *sp = stage + rl * EPI_PITCH + sgi * 8;
+                const v4f lo = *reinterpret_cast<const v4f *>(sp);
+                const v4f hi = *reinterpret_cast<const v4f *>(sp + 4);
+                const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                const int64_t o = (int64_t)row * N + col;
+                if (vec) {
+                    const v4i cw = cr[c][q];
+                    const int cwv[4] = {cw.x, cw.y, cw.z, cw.w};
+                    int w4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t u = (uint32_t)cwv[e];
+                        const float c0 = bf16_to_f32((uint16_t)(u & 0xffff)), c1 = bf16_to_f32((uint16_t)(u >> 16));
+                        w4[e] = (int)(f32_to_bf16_rne(v8[2 * e] + c0) |
+                                      ((uint32_t)f32_to_bf16_rne(v8[2 * e + 1] + c1) << 16));
+                    }
+                    *reinterpret_cast<v4i *>(D + o) = v4i{w4[0], w4[1], w4[2], w4[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (col + e < N) {
+                            float out = v8[e];
+                            if (C) out += bf16_to_f32(C[o + e]);
+                            D[o + e] = f32_to_bf16_rne(out);
+                        }
+                    }
+                }
+            }
+        });
+    });
+}
+
+bool pipe_eligible(const GemmProblem &p) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (int64_t)p.rows_a * p.K < lim && (int64_t)p.N * p.K < lim && p.ld_sfa >= 1;
+}
+
+// Launches pipe_kernel.  With SPLIT, `units` is the number of workgroups to
+// aim for: when it exceeds the number of tiles, the K steps of each tile are
+// split over about units/tiles workgroups (some tiles one more than others,
+// so that exactly `units` workgroups run), each split keeping at least one
+// step; otherwise, or when no workspace is available, there is no split.
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT>
+hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, std::string &config) {
+    PipeParams k;
+    k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.d = p.d; k.idx = p.idx;
+    k.rows_a = p.rows_a; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.G = p.G;
+    k.tiles_m = (p.rows_a + BM - 1) / BM;
+    k.tiles_n = (p.N + BN - 1) / BN;
+    k.gm = 4;
+    k.ws = nullptr;
+    k.counters = nullptr;
+    k.splits_lo = 1;
+    k.split_hi = 0;
+    k.slots = 1;
+    if ((p.K / kKBlock) % KS != 0) return hipErrorInvalidValue;
+    const int64_t groups = MODE == Mode::Masked ? p.G : 1;
+    const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n * groups;
+    const int nsteps = p.K / kKBlock / KS;
+    int64_t grid = tiles;
+    bool split = false;
+    if (SPLIT && units > tiles && nsteps > 1) {
+        int64_t lo = units / tiles, hi = units % tiles;
+        if (lo >= nsteps) {
+            lo = nsteps;
+            hi = 0;
+        } else if (lo + 1 > nsteps) {
+            hi = 0;
+        }
+        const int64_t slots = lo + (hi > 0 ? 1 : 0);
+        const size_t per = (size_t)BM * BN * sizeof(float);
+        if (slots > 1 && slots * BM * BN * 4 < ((int64_t)1 << 31) &&
+            get_splitk_workspace(stream, per * tiles * slots, (size_t)tiles, &k.ws, &k.counters)) {
+            k.splits_lo = (int)lo;
+            k.split_hi = (int)hi;
+            k.slots = (int)slots;
+            grid = hi * (lo + 1) + (tiles - hi) * lo;
+            split = true;
+        }
+    }
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    char buf[220];
+    snprintf(buf, sizeof buf,
+             "family=pipe mode=%d tile=%dx%dx128 waves=%dx%d stages=%d kblocks_per_stage=%d deep=%d splits=%d%s "
+             "grid=%lld",
+             (int)MODE, BM, BN, WGM, WGN, NST, KS, (int)DEEP, split ? k.splits_lo : 1,
+             split && k.split_hi > 0 ? "+" : "", (long long)grid);
+    config = buf;
+    if constexpr (SPLIT) {
+        if (split) {
+            hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true>), dim3((unsigned)grid),
+                               dim3(64 * WGM * WGN), 0, stream, k);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, false>), dim3((unsigned)grid),
+                           dim3(64 * WGM * WGN), 0, stream, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
+    if (!pipe_eligible(p)) return hipErrorInvalidValue;
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int nkb = p.K / kKBlock;
+    switch (p.mode) {
+    case Mode::Dense: {
+        // decode shapes: all rows in one tile row; K split over about one
+        // workgroup per CU (measured on MI355X for M in {64, 128} x
+        // (N, K) in {(2112, 7168), (7168, 16384)})
+        if (p.rows_a <= 64) {
+            if (nkb % 2 == 0) {
+                if (p.N < 4096) return launch_pipe_t<64, 64, 2, 4, 2, 2, false, Mode::Dense, true>(p, cus, stream, config);
+                return launch_pipe_t<64, 128, 2, 4, 3, 2, false, Mode::Dense, true>(p, cus, stream, config);
+            }
+            return launch_pipe_t<64, 128, 2, 4, 4, 1, false, Mode::Dense, true>(p, cus, stream, config);
+        }
+        if (p.rows_a <= 128) {
+            if (nkb % 2 == 0) {
+                if (p.N < 4096) return launch_pipe_t<128, 64, 4, 2, 3, 2, true, Mode::Dense, true>(p, cus, stream, config);
+                return launch_pipe_t<128, 128, 2, 4, 2, 2, true, Mode::Dense, true>(p, cus, stream, config);
+            }
+            return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true>(p, cus, stream, config);
+        }
+        return launch_pipe_t<256, 128, 4, 2, 3, 1, true, Mode::Dense, false>(p, 0, stream, config);
+    }
+    case Mode::Contig:   // expert segments are 128-row aligned: one expert per 128-row tile
+        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false>(p, 0, stream, config);
+    case Mode::Masked:
+        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false>(p, 0, stream, config);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dg
