@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from moe_grouped_gemm_scaled_amd import binding as dg  # noqa: E402
+from moe_grouped_gemm_scaled_amd import profiling  # noqa: E402
 from moe_grouped_gemm_scaled_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
@@ -231,6 +232,28 @@ def kernel_durations(jobs, reps=24):
     return out
 
 
+def measured_traffic(workload, jobs):
+    """HBM bytes moved by one launch of each GEMM of the step, summed, from the
+    committed counter summary profiles/hbm_traffic_<workload>.json (FETCH_SIZE
+    and WRITE_SIZE runs scaled by a copy of known size).  None when there is no
+    summary, when it misses a job, or when the kernel sources have changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_hash") != profiling.kernel_source_hash():
+        return None
+    total = 0.0
+    for j in jobs:
+        t = data.get("jobs", {}).get(j.name)
+        if not t:
+            return None
+        total += t["fetch_bytes"] + t["write_bytes"]
+    return round(total)
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
@@ -356,18 +379,21 @@ def main():
                 "gemm_TFLOPs": round(j.flops / (k / 1e3) / 1e12, 1), "config": cfg}
                for j, k, cfg in zip(jobs, kms, configs)]
 
+    traffic = measured_traffic(args.workload, jobs)
     if bound == "hbm":
         value = step_bytes / (ms_step / 1e3) / 1e9
         unit = "GB/s"
         achieved = gemm_bytes_total / gemm_time_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
         value = step_flops / (ms_step / 1e3) / 1e12
         unit = "TFLOP/s"
         achieved = step_flops / gemm_time_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+    # bytes the traffic figure compares with: the algorithmic bytes of the same launches
+    roof["algorithmic_bytes"] = round(gemm_bytes_total)
 
     cpu = None
     if not args.no_cpu_baseline:
