@@ -35,6 +35,7 @@
 // Without split-K, workgroups are numbered so that consecutive tiles of one
 // group run on the same XCD (shared L2) in a grouped raster.
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <atomic>
 
@@ -665,6 +666,12 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
             }
             return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true>(p, cus, stream, config);
         }
+        // prefill shapes.  Short K (few blocks per tile): 128x128 tiles on 8
+        // waves with two stages leave room for two workgroups per CU, so one
+        // workgroup's epilogue and pipeline fill overlap the other's MFMAs.
+        // Long K: 256x128 tiles with three stages (measured on MI355X for
+        // M = 4096 and (N, K) in {(4096, 7168), (7168, 2048), (24576, 1536)}).
+        if (nkb <= 16) return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
         return launch_pipe_t<256, 128, 4, 2, 3, 1, true, Mode::Dense, false>(p, 0, stream, config);
     }
     case Mode::Contig:   // expert segments are 128-row aligned: one expert per 128-row tile
