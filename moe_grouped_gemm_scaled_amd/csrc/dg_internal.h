@@ -41,6 +41,12 @@ hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, 
 bool pipe_eligible(const GemmProblem &p);
 hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
 
+// Persistent family (one workgroup per CU walking the tiles; stream-K for
+// dense decode shapes).  Returns an error, having launched nothing, when it
+// does not take the problem; the caller then picks another family.
+bool persist_eligible(const GemmProblem &p);
+hipError_t launch_persist(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
+
 // Split-K workspace of the calling device for `stream`: at least `ws_bytes`
 // of fp32 partials and `n_counters` zeroed arrival counters, grown on demand
 // (completed calls leave the counters zeroed).  Returns false when none large

@@ -272,7 +272,7 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
     return hipGetLastError();
 }
 
-// Kernel family override for tuning: DG_KERNEL_FAMILY=skinny|pipe|tiled picks
+// Kernel family override for tuning: DG_KERNEL_FAMILY=skinny|pipe|tiled|persist picks
 // that family wherever it supports the problem (read once per process).
 static int family_override() {
     static const int f = [] {
@@ -281,6 +281,7 @@ static int family_override() {
         if (!strcmp(e, "skinny")) return 1;
         if (!strcmp(e, "pipe")) return 2;
         if (!strcmp(e, "tiled")) return 3;
+        if (!strcmp(e, "persist")) return 4;
         return 0;
     }();
     return f;
@@ -290,6 +291,10 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
     const int f = family_override();
     if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
     if (f == 2 && pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);
+    if (f == 4 && persist_eligible(p)) {
+        const hipError_t e = launch_persist(p, num_cus, stream, config);
+        if (e != hipErrorInvalidValue && e != hipErrorNotReady) return e;
+    }
     if (f == 3) {
         switch (p.mode) {
         case Mode::Dense: return launch_tiled<128, 128, 2, 2, Mode::Dense>(p, stream, config);
@@ -303,6 +308,13 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
     const int cus = num_cus > 0 ? num_cus : 256;
     if (p.mode == Mode::Dense && p.rows_a <= 128 && skinny_eligible(p) && (int64_t)(p.N + 127) / 128 * 10 >= (int64_t)cus * 7)
         return launch_skinny(p, num_cus, stream, config);
+    // Masked layout: the persistent family deals only the row tiles with valid
+    // rows to the workgroups (measured on MI355X: 16 groups x 256 rows,
+    // N = 7168, K = 2048).
+    if (p.mode == Mode::Masked && persist_eligible(p)) {
+        const hipError_t e = launch_persist(p, num_cus, stream, config);
+        if (e != hipErrorInvalidValue && e != hipErrorNotReady) return e;
+    }
     if (pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);
     switch (p.mode) {
     case Mode::Dense:

@@ -24,7 +24,8 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["dg_device.h", "dg_internal.h", "gemm.hip", "decode.hip", "pipelined.hip", "quant.hip"]
+KERNEL_SOURCES = ["dg_device.h", "dg_internal.h", "dg_pipeline.h", "gemm.hip", "decode.hip", "pipelined.hip",
+                  "persistent.hip", "quant.hip"]
 
 
 def kernel_source_hash():
@@ -92,10 +93,10 @@ def _kernel_fragment(config):
     of a bench job's config string, as printed by the library."""
     kv = dict(tok.split("=", 1) for tok in config.split() if "=" in tok)
     fam, grid = kv["family"], int(kv["grid"])
-    if fam == "pipe":
+    if fam in ("pipe", "persist"):
         bm, bn = kv["tile"].split("x")[:2]
         wm, wn = kv["waves"].split("x")
-        frag = f"pipe_kernel<{bm}, {bn}, {wm}, {wn}, {kv['stages']}, {kv['kblocks_per_stage']}, "
+        frag = f"{fam}_kernel<{bm}, {bn}, {wm}, {wn}, {kv['stages']}, {kv['kblocks_per_stage']}, "
     elif fam == "skinny":
         wm, wn = kv["waves"].split("x")
         frag = (f"skinny_kernel<{int(kv['rows']) // 16}, {int(kv['cols']) // 16}, {wm}, {wn}, {kv['ks']}, "
