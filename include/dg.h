@@ -153,6 +153,16 @@ int dg_get_sf_aligned_size(int mn);
 int dg_set_num_cus(int n);
 int dg_get_num_cus(void);
 
+/* Kernel family used by the GEMM entry points, for tuning and testing:
+ * "auto" (the default: chosen per problem), "pipe", "persist", "skinny" or
+ * "tiled".  A family that cannot take a problem falls back to the automatic
+ * choice; results are the same whichever family runs (within the documented
+ * tolerance).  The initial value comes from the environment variable
+ * DG_KERNEL_FAMILY.  set returns DG_ERR_NULL or DG_ERR_ARG for a NULL or
+ * unknown name; get returns the name in force (process-wide setting). */
+int dg_set_kernel_family(const char *name);
+const char *dg_get_kernel_family(void);
+
 /* Static string for a status code. */
 const char *dg_status_string(int status);
 

@@ -43,6 +43,8 @@ EXPORTS = {
     "dg_get_sf_aligned_size": (ct.c_int, [ct.c_int]),
     "dg_set_num_cus": (ct.c_int, [ct.c_int]),
     "dg_get_num_cus": (ct.c_int, []),
+    "dg_set_kernel_family": (ct.c_int, [ct.c_char_p]),
+    "dg_get_kernel_family": (ct.c_char_p, []),
     "dg_status_string": (ct.c_char_p, [ct.c_int]),
     "dg_last_config": (ct.c_char_p, []),
 }
@@ -197,6 +199,15 @@ def get_num_cus() -> int:
     if v < 0:
         raise DGError(v, "dg_get_num_cus")
     return v
+
+
+def set_kernel_family(name: str):
+    """Kernel family of the GEMM entry points: auto, pipe, persist, skinny or tiled."""
+    _check(lib().dg_set_kernel_family(name.encode()), "dg_set_kernel_family")
+
+
+def get_kernel_family() -> str:
+    return lib().dg_get_kernel_family().decode()
 
 
 def last_config() -> str:

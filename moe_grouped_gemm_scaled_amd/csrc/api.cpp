@@ -153,6 +153,18 @@ int dg_get_num_cus(void) {
     return cus;
 }
 
+int dg_set_kernel_family(const char *name) {
+    if (!name) return DG_ERR_NULL;
+    const int f = dg::kernel_family_from_name(name);
+    if (f < 0) return DG_ERR_ARG;
+    dg::kernel_family_setting().store(f, std::memory_order_relaxed);
+    return DG_OK;
+}
+
+const char *dg_get_kernel_family(void) {
+    return dg::kernel_family_name(dg::kernel_family_setting().load(std::memory_order_relaxed));
+}
+
 const char *dg_status_string(int status) {
     switch (status) {
     case DG_OK: return "DG_OK";

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <string>
 
 namespace dg {
@@ -53,6 +54,11 @@ hipError_t launch_persist(const GemmProblem &p, int num_cus, hipStream_t stream,
 // enough exists and none may be allocated now (the stream is being captured
 // into a graph); the caller then runs without split-K.
 bool get_splitk_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters, float **ws, int **counters);
+
+// Kernel family setting shared by the entry points (see dg_set_kernel_family).
+int kernel_family_from_name(const char *name);
+const char *kernel_family_name(int f);
+std::atomic<int> &kernel_family_setting();
 
 // Chooses a kernel configuration, launches it on `stream`, and describes the
 // choice in `config`.  Returns the HIP error of the launch.

@@ -22,6 +22,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -272,23 +274,29 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
     return hipGetLastError();
 }
 
-// Kernel family override for tuning: DG_KERNEL_FAMILY=skinny|pipe|tiled|persist picks
-// that family wherever it supports the problem (read once per process).
-static int family_override() {
-    static const int f = [] {
+// Kernel family setting (0 = automatic, 1 skinny, 2 pipe, 3 tiled, 4
+// persist); initialised from DG_KERNEL_FAMILY, changed by dg_set_kernel_family.
+static const char *const kFamilyNames[] = {"auto", "skinny", "pipe", "tiled", "persist"};
+
+int kernel_family_from_name(const char *name) {
+    for (int i = 0; i < 5; ++i)
+        if (!strcmp(name, kFamilyNames[i])) return i;
+    return -1;
+}
+
+const char *kernel_family_name(int f) { return f >= 0 && f < 5 ? kFamilyNames[f] : "auto"; }
+
+std::atomic<int> &kernel_family_setting() {
+    static std::atomic<int> f([] {
         const char *e = getenv("DG_KERNEL_FAMILY");
-        if (!e) return 0;
-        if (!strcmp(e, "skinny")) return 1;
-        if (!strcmp(e, "pipe")) return 2;
-        if (!strcmp(e, "tiled")) return 3;
-        if (!strcmp(e, "persist")) return 4;
-        return 0;
-    }();
+        const int v = e ? kernel_family_from_name(e) : 0;
+        return v < 0 ? 0 : v;
+    }());
     return f;
 }
 
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
-    const int f = family_override();
+    const int f = kernel_family_setting().load(std::memory_order_relaxed);
     if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
     if (f == 2 && pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);
     if (f == 4 && persist_eligible(p)) {

@@ -52,6 +52,19 @@ def test_utilities(lib):
         assert lib.dg_status_string(s).decode().startswith(("DG_OK", "DG_ERR"))
 
 
+def test_kernel_family_setting(lib):
+    start = lib.dg_get_kernel_family().decode()
+    try:
+        for name in ("pipe", "persist", "skinny", "tiled", "auto"):
+            assert lib.dg_set_kernel_family(name.encode()) == 0
+            assert lib.dg_get_kernel_family().decode() == name
+        assert lib.dg_set_kernel_family(b"cutlass") == -4
+        assert lib.dg_set_kernel_family(None) == -1
+        assert lib.dg_get_kernel_family().decode() == "auto"
+    finally:
+        lib.dg_set_kernel_family(start.encode())
+
+
 def test_dense_argument_errors(lib):
     f = lib.dg_fp8_gemm_nt
     # a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream
