@@ -308,21 +308,11 @@ skinny_kernel(SkinnyParams p) {
     if (S > 1) {
         __shared__ int is_last;
         constexpr int PART = ROWS * BN;                      // floats per (tile, split)
-        constexpr int CPOL_COHERENT = 16;                    // sc1
         const __amdgpu_buffer_rsrc_t rW =
             __builtin_amdgcn_make_buffer_rsrc((void *)(p.ws + (int64_t)tile_id * S * PART), (short)0,
                                               S * PART * 4, 0x00020000);
         const int base = (wave * (MTW * NTWW * 64) + lane) * 16;   // bytes
-        static_for<MTW>([&](auto ic) __attribute__((always_inline)) {
-            constexpr int i = decltype(ic)::value;
-            static_for<NTWW>([&](auto jc) __attribute__((always_inline)) {
-                constexpr int j = decltype(jc)::value;
-                const v4f a4 = acc[i][j];
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, a4), rW,
-                                                       base + (i * NTWW + j) * 64 * 16, s * PART * 4,
-                                                       CPOL_COHERENT);
-            });
-        });
+        publish_partial(acc, rW, base, PART * 4, s);
         __builtin_amdgcn_s_waitcnt(0);                  // partial stores complete before the count
         __syncthreads();
         if (tid == 0)
@@ -330,36 +320,7 @@ skinny_kernel(SkinnyParams p) {
                       S - 1;
         __syncthreads();
         if (!is_last) return;
-        v4f sum[MTW][NTWW];
-        static_for<MTW>([&](auto ic) __attribute__((always_inline)) {
-            static_for<NTWW>([&](auto jc) __attribute__((always_inline)) {
-                sum[decltype(ic)::value][decltype(jc)::value] = v4f{0.f, 0.f, 0.f, 0.f};
-            });
-        });
-        for (int s2 = 0; s2 < S; ++s2) {
-            v4f part[MTW][NTWW];
-            static_for<MTW>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int i = decltype(ic)::value;
-                static_for<NTWW>([&](auto jc) __attribute__((always_inline)) {
-                    constexpr int j = decltype(jc)::value;
-                    part[i][j] = __builtin_bit_cast(
-                        v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, base + (i * NTWW + j) * 64 * 16, s2 * PART * 4,
-                                                                   CPOL_COHERENT));
-                });
-            });
-            static_for<MTW>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int i = decltype(ic)::value;
-                static_for<NTWW>([&](auto jc) __attribute__((always_inline)) {
-                    constexpr int j = decltype(jc)::value;
-                    sum[i][j] += s2 == s ? acc[i][j] : part[i][j];
-                });
-            });
-        }
-        static_for<MTW>([&](auto ic) __attribute__((always_inline)) {
-            static_for<NTWW>([&](auto jc) __attribute__((always_inline)) {
-                acc[decltype(ic)::value][decltype(jc)::value] = sum[decltype(ic)::value][decltype(jc)::value];
-            });
-        });
+        sum_partials(acc, rW, base, PART * 4, S, s);
         if (tid == 0) __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 

@@ -37,8 +37,18 @@ __device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i &a, const v8i &b, c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Promotion of a block partial: acc + p * s, element-wise, as whole-vector
-// values (element stores into an accumulator array would keep it in memory).
+// Promotion of a block partial: acc + p * s, as whole-vector values
+// (element stores into an accumulator array would keep it in memory); one
+// scale for all four elements, or one each.
+__device__ __forceinline__ v4f promote(const v4f &acc, const v4f &p, float s) {
+    v4f r;
+    r.x = __builtin_fmaf(p.x, s, acc.x);
+    r.y = __builtin_fmaf(p.y, s, acc.y);
+    r.z = __builtin_fmaf(p.z, s, acc.z);
+    r.w = __builtin_fmaf(p.w, s, acc.w);
+    return r;
+}
+
 __device__ __forceinline__ v4f promote(const v4f &acc, const v4f &p, const v4f &s) {
     v4f r;
     r.x = __builtin_fmaf(p.x, s.x, acc.x);
@@ -46,6 +56,78 @@ __device__ __forceinline__ v4f promote(const v4f &acc, const v4f &p, const v4f &
     r.z = __builtin_fmaf(p.z, s.z, acc.z);
     r.w = __builtin_fmaf(p.w, s.w, acc.w);
     return r;
+}
+
+// Split-K exchange of one tile's fp32 partials.  The workspace region `ws`
+// (a buffer resource) holds one slot per split, `slot_bytes` apart; a wave
+// stores its SM x SN fragments as consecutive 1 KB chunks from byte `base`
+// of a slot (16 bytes per lane), with device-coherent (sc1) stores so that
+// a workgroup on another XCD reads them from memory, not from its own L2.
+constexpr int kCpolCoherent = 16;   // sc1
+
+template <int SM, int SN>
+__device__ __forceinline__ void publish_partial(const v4f (&acc)[SM][SN], __amdgpu_buffer_rsrc_t ws, int base,
+                                                int slot_bytes, int s) {
+    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), ws, base + (i * SN + j) * 1024,
+                                                   s * slot_bytes, kCpolCoherent);
+        });
+    });
+}
+
+// The last split to arrive replaces its accumulators by the sum of all S
+// partials, added in split order (its own from registers, the others loaded).
+// The loads of RB slots are issued together before any is added, so the
+// exchange costs about ceil(S / RB) memory round trips instead of S.  A batch
+// holds at most MAXV fragments (4 registers each).
+template <int MAXV = 32, int SM, int SN>
+__device__ __forceinline__ void sum_partials(v4f (&acc)[SM][SN], __amdgpu_buffer_rsrc_t ws, int base,
+                                             int slot_bytes, int S, int s) {
+    constexpr int RB = MAXV / (SM * SN) < 1 ? 1 : (MAXV / (SM * SN) > 8 ? 8 : MAXV / (SM * SN));
+    v4f sum[SM][SN];
+    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+            sum[decltype(ic)::value][decltype(jc)::value] = v4f{0.f, 0.f, 0.f, 0.f};
+        });
+    });
+    for (int s0 = 0; s0 < S; s0 += RB) {
+        v4f part[RB][SM][SN];
+        static_for<RB>([&](auto bc) __attribute__((always_inline)) {
+            constexpr int b = decltype(bc)::value;
+            const int s2 = s0 + b;
+            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    part[b][i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                    if (s2 < S && s2 != s)   // uniform
+                        part[b][i][j] = __builtin_bit_cast(
+                            v4f, __builtin_amdgcn_raw_buffer_load_b128(ws, base + (i * SN + j) * 1024,
+                                                                       s2 * slot_bytes, kCpolCoherent));
+                });
+            });
+        });
+        static_for<RB>([&](auto bc) __attribute__((always_inline)) {
+            constexpr int b = decltype(bc)::value;
+            if (s0 + b < S) {
+                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+                    constexpr int i = decltype(ic)::value;
+                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                        constexpr int j = decltype(jc)::value;
+                        sum[i][j] += s0 + b == s ? acc[i][j] : part[b][i][j];
+                    });
+                });
+            }
+        });
+    }
+    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+            acc[decltype(ic)::value][decltype(jc)::value] = sum[decltype(ic)::value][decltype(jc)::value];
+        });
+    });
 }
 
 // fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet).

@@ -13,11 +13,15 @@
 //    workgroups in grouped-raster order, numbered so that the tiles in flight
 //    on one XCD are neighbours;
 //  - stream-K mode (dense decode shapes): the (tile, K step) pairs are laid
-//    out tile by tile and every workgroup takes one contiguous, equal share.
-//    A tile cut between workgroups is finished by the last of them to
-//    arrive: each publishes its fp32 partial (device-coherent stores), bumps
-//    the tile's counter, and the last one sums the partials in workgroup
-//    order (the same result whatever the arrival order) and writes D.
+//    out tile by tile and every workgroup takes one contiguous, equal share
+//    of at most one tile's steps, so a share covers the end of one tile and
+//    the start of the next at most.  A tile cut between workgroups is
+//    finished by the last of them to arrive: each publishes its fp32 partial
+//    (device-coherent stores), bumps the tile's counter, and the last one
+//    sums the partials in workgroup order (the same result whatever the
+//    arrival order) and writes D.  A share that crosses a tile boundary keeps
+//    the first tile's sums in registers and publishes both at the end of the
+//    share, so the stream of loads never waits for a publication.
 // The producer side of a wave (DMA of step j + NST - 1) and its consumer side
 // (multiply step j) are decoupled by a small record stored with every stage
 // (tile, step, flags), written when the stage's DMA is issued: the consumer
@@ -50,6 +54,7 @@ constexpr int kMaxRowTiles = 1024;   // capacity of the (group, row tile) list o
 constexpr int kMetaCompute = 1;      // the step is to be multiplied
 constexpr int kMetaLast = 2;         // ... and is the last step of its tile or share
 constexpr int kMetaEnd = 4;          // no work from here on
+constexpr int kMetaShareEnd = 8;     // stream-K: the last step of this workgroup's share
 
 // Steps U, U+1, .. of one round, nested: step U + 1 runs only if step U
 // returned true (see nested_steps for why the conditions are nested).
@@ -270,8 +275,9 @@ persist_kernel(PersistParams p) {
     // flags of the step the producer is about to fetch
     auto producer_flags = [&]() __attribute__((always_inline)) -> int {
         if (p_done) return kMetaEnd;
-        const bool last = p_s == nsteps - 1 || (STREAMK && q == q_end - 1);
-        return kMetaCompute | (last ? kMetaLast : 0);
+        const bool share_end = STREAMK && q == q_end - 1;
+        const bool last = p_s == nsteps - 1 || share_end;
+        return kMetaCompute | (last ? kMetaLast : 0) | (share_end ? kMetaShareEnd : 0);
     };
     auto advance = [&]() __attribute__((always_inline)) {
         if (p_done) return;                        // keep re-fetching the last step (never multiplied)
@@ -306,22 +312,20 @@ persist_kernel(PersistParams p) {
     };
     zero_acc();
     const int wave_nb = ((wn * TN) / 128) < NBW ? (wn * TN) / 128 : 0;
-    int off_b[SN][2], off_a[SM][2], off_sa[SM];
-    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-        constexpr int j = decltype(jc)::value;
-        const int row = (wn * SN + j) * 16 + l16;
-        off_b[j][0] = opaque_offset(OFF_B + row * kKBlock + ((g4 ^ (row & 7)) << 4));
-        off_b[j][1] = opaque_offset(OFF_B + row * kKBlock + (((g4 + 4) ^ (row & 7)) << 4));
-    });
-    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        const int row = (wm * SM + i) * 16 + l16;
-        off_a[i][0] = opaque_offset(row * kKBlock + ((g4 ^ (row & 7)) << 4));
-        off_a[i][1] = opaque_offset(row * kKBlock + (((g4 + 4) ^ (row & 7)) << 4));
-        off_sa[i] = opaque_offset(OFF_SA + ((wm * SM + i) * 16 + 4 * g4) * 4);
-    });
+    // offsets of subtile 0 (subtile i, j: + 2 KB each, same swizzle)
+    int off_b0[2], off_a0[2], off_sa0;
+    {
+        const int rowb = wn * SN * 16 + l16, rowa = wm * SM * 16 + l16;
+        off_b0[0] = opaque_offset(OFF_B + rowb * kKBlock + ((g4 ^ (l16 & 7)) << 4));
+        off_b0[1] = opaque_offset(OFF_B + rowb * kKBlock + (((g4 + 4) ^ (l16 & 7)) << 4));
+        off_a0[0] = opaque_offset(rowa * kKBlock + ((g4 ^ (l16 & 7)) << 4));
+        off_a0[1] = opaque_offset(rowa * kKBlock + (((g4 + 4) ^ (l16 & 7)) << 4));
+        off_sa0 = opaque_offset(OFF_SA + rowa * 4);
+    }
     const int off_sb = OFF_SB + 16 * wave_nb;
 
+    // transposed block partials: lane l holds row 16i + l%16 and columns
+    // 16j + 4(l/16) .. +3 (B fragment as the MFMA's first operand)
     auto compute_block = [&](const uint8_t *stg_step, auto kkc) __attribute__((always_inline)) {
         constexpr int kk = decltype(kkc)::value;
         const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
@@ -331,22 +335,22 @@ persist_kernel(PersistParams p) {
         v8i bf[SN];
         static_for<SN>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b[j][0]);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b[j][1]);
+            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b0[0] + j * 16 * kKBlock);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b0[1] + j * 16 * kKBlock);
             bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         });
-        auto read_a = [&](auto ic, v8i &af, v4f &sa) __attribute__((always_inline)) {
+        auto read_a = [&](auto ic, v8i &af, float &sa) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a[i][0]);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a[i][1]);
+            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a0[0] + i * 16 * kKBlock);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
             af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            sa = *reinterpret_cast<const v4f *>(stg_s + off_sa[i]);
+            sa = *reinterpret_cast<const float *>(stg_s + off_sa0 + i * 64);
         };
         v8i af_cur, af_nxt;
-        v4f sa_cur, sa_nxt;
+        float sa_cur, sa_nxt;
         read_a(std::integral_constant<int, 0>{}, af_cur, sa_cur);
         if constexpr (DEEP) {
-            v4f sa_prv;
+            float sa_prv;
             v4f pp_prv[SN];
             static_for<SM>([&](auto ic) __attribute__((always_inline)) {
                 constexpr int i = decltype(ic)::value;
@@ -354,10 +358,10 @@ persist_kernel(PersistParams p) {
                 v4f pp[SN];
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
-                    pp[j] = mfma_16x16x128_e4m3(af_cur, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+                    pp[j] = mfma_16x16x128_e4m3(bf[j], af_cur, v4f{0.f, 0.f, 0.f, 0.f});
                 });
                 if constexpr (i > 0) {
-                    const v4f sv = v4f{sa_prv.x * sb, sa_prv.y * sb, sa_prv.z * sb, sa_prv.w * sb};
+                    const float sv = sa_prv * sb;
                     static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                         constexpr int j = decltype(jc)::value;
                         acc[i - 1][j] = promote(acc[i - 1][j], pp_prv[j], sv);
@@ -372,7 +376,7 @@ persist_kernel(PersistParams p) {
                     sa_cur = sa_nxt;
                 }
             });
-            const v4f sv = v4f{sa_prv.x * sb, sa_prv.y * sb, sa_prv.z * sb, sa_prv.w * sb};
+            const float sv = sa_prv * sb;
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
                 acc[SM - 1][j] = promote(acc[SM - 1][j], pp_prv[j], sv);
@@ -384,9 +388,9 @@ persist_kernel(PersistParams p) {
                 v4f pp[SN];
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
-                    pp[j] = mfma_16x16x128_e4m3(af_cur, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+                    pp[j] = mfma_16x16x128_e4m3(bf[j], af_cur, v4f{0.f, 0.f, 0.f, 0.f});
                 });
-                const v4f sv = v4f{sa_cur.x * sb, sa_cur.y * sb, sa_cur.z * sb, sa_cur.w * sb};
+                const float sv = sa_cur * sb;
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
                     acc[i][j] = promote(acc[i][j], pp[j], sv);
@@ -456,9 +460,8 @@ persist_kernel(PersistParams p) {
                 constexpr int i = c * (EPI_ROWS / 16) + ii;
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
-                    const v4f a4 = acc[i][j];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) stage[(ii * 16 + 4 * g4 + v) * EPI_PITCH + j * 16 + l16] = a4[v];
+                    // row 16i + l%16, columns 16j + 4(l/16) .. +3
+                    *reinterpret_cast<v4f *>(stage + (ii * 16 + l16) * EPI_PITCH + j * 16 + 4 * g4) = acc[i][j];
                 });
             });
             static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
@@ -503,73 +506,94 @@ persist_kernel(PersistParams p) {
         });
     };
 
-    // ---- finishing tile k after its last step here.  Tiled, or a share that
-    // covers the whole tile: the epilogue.  Otherwise publish the partial; the
-    // last share to arrive sums all of them and does the epilogue.
+    // ---- finishing tile k after its last step here.  Tiled: the epilogue.
+    // Stream-K: at a tile's last step inside the share the sums are kept in
+    // acc_prev (no memory traffic); at the share's last step each tile of the
+    // share is written directly if the share covers it whole, otherwise its
+    // partial is published, and after one wait for all stores both tiles are
+    // counted; the last share to arrive at a tile sums its partials and does
+    // its epilogue.
+    v4f acc_prev[SM][SN];
+    int k_prev = -1;
+    auto copy_acc = [&](v4f (&dst)[SM][SN], const v4f (&src)[SM][SN]) __attribute__((always_inline)) {
+        static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                dst[decltype(ic)::value][decltype(jc)::value] = src[decltype(ic)::value][decltype(jc)::value];
+            });
+        });
+    };
+    // first and last workgroup whose share holds steps of tile k
+    auto sharers = [&](int k, int &gf, int &gl) __attribute__((always_inline)) {
+        const int64_t Q0 = (int64_t)k * nsteps, Q1 = Q0 + nsteps - 1;
+        gf = (int)(((Q0 + 1) * Gw + units - 1) / units) - 1;
+        gl = (int)(((Q1 + 1) * Gw + units - 1) / units) - 1;
+    };
     auto finish = [&](int k, uint8_t *stg) __attribute__((always_inline)) {
+        if constexpr (STREAMK) {                   // the share goes on into tile k + 1
+            copy_acc(acc_prev, acc);
+            k_prev = k;
+        } else {
+            lds_barrier();                         // every wave is done reading stg
+            epi_write(stg);
+        }
+    };
+    // The end of a stream-K share, once, after the main loop (its code is
+    // large, and inside the unrolled loop it would be repeated per stage).
+    auto finish_share = [&](int k, uint8_t *stg) __attribute__((always_inline)) {
         lds_barrier();                             // every wave is done reading stg
         if constexpr (STREAMK) {
-            const int64_t Q0 = (int64_t)k * nsteps, Q1 = Q0 + nsteps - 1;
-            const int g_first = (int)(((Q0 + 1) * Gw + units - 1) / units) - 1;
-            const int g_last = (int)(((Q1 + 1) * Gw + units - 1) / units) - 1;
-            if (g_first != g_last) {
-                constexpr int PART = BM * BN;
-                constexpr int CPOL_COHERENT = 16;  // sc1
-                const int nseg = g_last - g_first + 1;
-                const int my = g - g_first;
-                const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(p.ws + (int64_t)k * p.slots * PART), (short)0, nseg * PART * 4, 0x00020000);
-                const int base = (wave * (SM * SN * 64) + lane) * 16;
-                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                    constexpr int i = decltype(ic)::value;
-                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                        constexpr int j = decltype(jc)::value;
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), rW,
-                                                               base + (i * SN + j) * 64 * 16, my * PART * 4,
-                                                               CPOL_COHERENT);
-                    });
-                });
-                __builtin_amdgcn_s_waitcnt(0);     // the partial is stored before it is counted
+            constexpr int PART = BM * BN;
+            const int base = (wave * (SM * SN * 64) + lane) * 16;
+            int gf1, gl1, gf0 = 0, gl0 = 0;
+            sharers(k, gf1, gl1);
+            const bool has0 = k_prev >= 0;
+            if (has0) sharers(k_prev, gf0, gl0);
+            const bool sh1 = gf1 != gl1, sh0 = has0 && gf0 != gl0;
+            const int n1 = gl1 - gf1 + 1, n0 = gl0 - gf0 + 1;
+            const __amdgpu_buffer_rsrc_t rW1 = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.ws + (int64_t)k * p.slots * PART), (short)0, n1 * PART * 4, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rW0 = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.ws + (int64_t)(has0 ? k_prev : 0) * p.slots * PART), (short)0, n0 * PART * 4,
+                0x00020000);
+            int last = 0;                          // bit 0: finish tile k_prev here; bit 1: tile k
+            if (sh0 || sh1) {
+                if (sh0) publish_partial(acc_prev, rW0, base, PART * 4, g - gf0);
+                if (sh1) publish_partial(acc, rW1, base, PART * 4, g - gf1);
+                __builtin_amdgcn_s_waitcnt(0);     // the partials are stored before they are counted
                 __syncthreads();
-                if (tid == 0)
-                    is_last_sh = __hip_atomic_fetch_add(p.counters + k, 1, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT) == nseg - 1;
-                __syncthreads();
-                if (!is_last_sh) return;
-                v4f sum[SM][SN];
-                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                        sum[decltype(ic)::value][decltype(jc)::value] = v4f{0.f, 0.f, 0.f, 0.f};
-                    });
-                });
-                for (int s2 = 0; s2 < nseg; ++s2) {
-                    v4f part[SM][SN];
-                    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                        constexpr int i = decltype(ic)::value;
-                        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                            constexpr int j = decltype(jc)::value;
-                            part[i][j] = __builtin_bit_cast(
-                                v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, base + (i * SN + j) * 64 * 16,
-                                                                           s2 * PART * 4, CPOL_COHERENT));
-                        });
-                    });
-                    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                        constexpr int i = decltype(ic)::value;
-                        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                            constexpr int j = decltype(jc)::value;
-                            sum[i][j] += s2 == my ? acc[i][j] : part[i][j];
-                        });
-                    });
+                if (tid == 0) {
+                    int f = 0;
+                    if (sh0 && __hip_atomic_fetch_add(p.counters + k_prev, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) == n0 - 1)
+                        f |= 1;
+                    if (sh1 && __hip_atomic_fetch_add(p.counters + k, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) == n1 - 1)
+                        f |= 2;
+                    is_last_sh = f;
                 }
-                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                        acc[decltype(ic)::value][decltype(jc)::value] = sum[decltype(ic)::value][decltype(jc)::value];
-                    });
-                });
-                if (tid == 0) __hip_atomic_store(p.counters + k, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                last = __builtin_amdgcn_readfirstlane(is_last_sh);
+            }
+            if (!sh0) last |= has0 ? 1 : 0;
+            if (!sh1) last |= 2;
+            if (last & 2) {                        // tile k (its C is loaded already)
+                if (sh1) {
+                    sum_partials<16>(acc, rW1, base, PART * 4, n1, g - gf1);
+                    if (tid == 0) __hip_atomic_store(p.counters + k, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                epi_write(stg);
+            }
+            if (last & 1) {                        // tile k_prev
+                copy_acc(acc, acc_prev);
+                if (sh0) {
+                    sum_partials<16>(acc, rW0, base, PART * 4, n0, g - gf0);
+                    if (tid == 0)
+                        __hip_atomic_store(p.counters + k_prev, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                epi_prepare(k_prev);
+                epi_write(stg);
             }
         }
-        epi_write(stg);
     };
 
     auto dma = [&](uint8_t *stg) __attribute__((always_inline)) {
@@ -586,6 +610,8 @@ persist_kernel(PersistParams p) {
     // (or the share's) last step.
     if (tid < NST) meta_sh[tid] = v4i{0, 0, 0, 0};
     __syncthreads();
+    int end_k = -1;                                // stream-K: the tile whose step ended the share
+    uint8_t *end_stg = stage0;
     constexpr int kWaitPipe = wait_vmcnt((NST - 2) * PER_STEP);
 #pragma clang loop unroll(disable)
     for (;;) {
@@ -608,6 +634,11 @@ persist_kernel(PersistParams p) {
             if (c_flags & kMetaCompute) {
                 compute(src);
                 if (c_last) {
+                    if (STREAMK && (c_flags & kMetaShareEnd)) {
+                        end_k = c_k;
+                        end_stg = src;
+                        return false;
+                    }
                     finish(c_k, src);
                     zero_acc();
                 }
@@ -617,6 +648,7 @@ persist_kernel(PersistParams p) {
         if (!more) break;
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if (STREAMK && end_k >= 0) finish_share(end_k, end_stg);
 }
 
 bool persist_eligible(const GemmProblem &p) {

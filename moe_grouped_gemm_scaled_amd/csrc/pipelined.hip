@@ -242,31 +242,32 @@ pipe_kernel(PipeParams p) {
     });
     const int wave_nb = ((wn * TN) / 128) < NBW ? (wn * TN) / 128 : 0;
 
-    // Byte offsets within a stage of the fragments this lane reads: the two
-    // 16-byte halves of B subtile j and A subtile i, and the A scales of
-    // subtile i.  Each is made opaque to the optimiser, so that every LDS read
-    // is one address computation from its stage object: the compiler can then
-    // tell which stage a read touches and adds no waits for DMA into other
-    // stages.
-    int off_b[SN][2], off_a[SM][2], off_sa[SM];
-    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-        constexpr int j = decltype(jc)::value;
-        const int row = (wn * SN + j) * 16 + l16;
-        off_b[j][0] = opaque_offset(OFF_B + row * kKBlock + ((g4 ^ (row & 7)) << 4));
-        off_b[j][1] = opaque_offset(OFF_B + row * kKBlock + (((g4 + 4) ^ (row & 7)) << 4));
-    });
-    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        const int row = (wm * SM + i) * 16 + l16;
-        off_a[i][0] = opaque_offset(row * kKBlock + ((g4 ^ (row & 7)) << 4));
-        off_a[i][1] = opaque_offset(row * kKBlock + (((g4 + 4) ^ (row & 7)) << 4));
-        off_sa[i] = opaque_offset(OFF_SA + ((wm * SM + i) * 16 + 4 * g4) * 4);
-    });
+    // Byte offsets within a stage of the fragments this lane reads for
+    // subtile 0: the two 16-byte halves of B subtile 0 and A subtile 0, and
+    // the A scale of the lane's row.  Subtile i (j) lies 16 rows = 2 KB
+    // further on with the same swizzle (it depends on row & 7 only), so its
+    // reads use the same register plus a constant.  The offsets are opaque to
+    // the optimiser, so that every LDS read is one address computation from
+    // its stage object: the compiler can then tell which stage a read touches
+    // and adds no waits for DMA into other stages.
+    int off_b0[2], off_a0[2], off_sa0;
+    {
+        const int rowb = wn * SN * 16 + l16, rowa = wm * SM * 16 + l16;
+        off_b0[0] = opaque_offset(OFF_B + rowb * kKBlock + ((g4 ^ (l16 & 7)) << 4));
+        off_b0[1] = opaque_offset(OFF_B + rowb * kKBlock + (((g4 + 4) ^ (l16 & 7)) << 4));
+        off_a0[0] = opaque_offset(rowa * kKBlock + ((g4 ^ (l16 & 7)) << 4));
+        off_a0[1] = opaque_offset(rowa * kKBlock + (((g4 + 4) ^ (l16 & 7)) << 4));
+        off_sa0 = opaque_offset(OFF_SA + rowa * 4);
+    }
     const int off_sb = OFF_SB + 16 * wave_nb;
 
-    // Multiply K block kk of the step held in `stg`.  Software pipeline over
-    // the wave's row subtiles: the A fragment of subtile i+1 is read while the
-    // MFMAs of subtile i run; with DEEP, subtile i-1 is also promoted then.
+    // Multiply K block kk of the step held in `stg`.  The MFMA takes the B
+    // fragment as its first operand, so it yields the transposed block
+    // partial: lane l holds row 16i + l%16 of the subtile and its columns
+    // 16j + 4(l/16) .. +3, and the row's scale sfa*sfb is one number per lane.
+    // Software pipeline over the wave's row subtiles: the A fragment of
+    // subtile i+1 is read while the MFMAs of subtile i run; with DEEP,
+    // subtile i-1 is also promoted then.
     auto compute_block = [&](const uint8_t *stg_step, auto kkc) __attribute__((always_inline)) {
         constexpr int kk = decltype(kkc)::value;
         const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
@@ -276,23 +277,23 @@ pipe_kernel(PipeParams p) {
         v8i bf[SN];
         static_for<SN>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b[j][0]);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b[j][1]);
+            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b0[0] + j * 16 * kKBlock);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b0[1] + j * 16 * kKBlock);
             bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         });
-        auto read_a = [&](auto ic, v8i &af, v4f &sa) __attribute__((always_inline)) {
+        auto read_a = [&](auto ic, v8i &af, float &sa) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a[i][0]);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a[i][1]);
+            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a0[0] + i * 16 * kKBlock);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
             af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            sa = *reinterpret_cast<const v4f *>(stg_s + off_sa[i]);
+            sa = *reinterpret_cast<const float *>(stg_s + off_sa0 + i * 64);
         };
         v8i af_cur, af_nxt;
-        v4f sa_cur, sa_nxt;
+        float sa_cur, sa_nxt;
         read_a(std::integral_constant<int, 0>{}, af_cur, sa_cur);
         if constexpr (DEEP) {
             // promote subtile i-1 while the MFMAs of subtile i run (two sets of partials live)
-            v4f sa_prv;
+            float sa_prv;
             v4f pp_prv[SN];
             static_for<SM>([&](auto ic) __attribute__((always_inline)) {
                 constexpr int i = decltype(ic)::value;
@@ -300,10 +301,10 @@ pipe_kernel(PipeParams p) {
                 v4f pp[SN];
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
-                    pp[j] = mfma_16x16x128_e4m3(af_cur, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+                    pp[j] = mfma_16x16x128_e4m3(bf[j], af_cur, v4f{0.f, 0.f, 0.f, 0.f});
                 });
                 if constexpr (i > 0) {
-                    const v4f sv = v4f{sa_prv.x * sb, sa_prv.y * sb, sa_prv.z * sb, sa_prv.w * sb};
+                    const float sv = sa_prv * sb;
                     static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                         constexpr int j = decltype(jc)::value;
                         acc[i - 1][j] = promote(acc[i - 1][j], pp_prv[j], sv);
@@ -318,7 +319,7 @@ pipe_kernel(PipeParams p) {
                     sa_cur = sa_nxt;
                 }
             });
-            const v4f sv = v4f{sa_prv.x * sb, sa_prv.y * sb, sa_prv.z * sb, sa_prv.w * sb};
+            const float sv = sa_prv * sb;
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
                 acc[SM - 1][j] = promote(acc[SM - 1][j], pp_prv[j], sv);
@@ -332,9 +333,9 @@ pipe_kernel(PipeParams p) {
                 v4f pp[SN];
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
-                    pp[j] = mfma_16x16x128_e4m3(af_cur, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+                    pp[j] = mfma_16x16x128_e4m3(bf[j], af_cur, v4f{0.f, 0.f, 0.f, 0.f});
                 });
-                const v4f sv = v4f{sa_cur.x * sb, sa_cur.y * sb, sa_cur.z * sb, sa_cur.w * sb};
+                const float sv = sa_cur * sb;
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
                     acc[i][j] = promote(acc[i][j], pp[j], sv);
@@ -380,20 +381,11 @@ pipe_kernel(PipeParams p) {
         if (S > 1) {
             __shared__ int is_last;
             constexpr int PART = BM * BN;                    // floats per (tile, split)
-            constexpr int CPOL_COHERENT = 16;                // sc1
             const __amdgpu_buffer_rsrc_t rW =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(p.ws + (int64_t)t_all * p.slots * PART), (short)0,
                                                   S * PART * 4, 0x00020000);
             const int base = (wave * (SM * SN * 64) + lane) * 16;   // bytes, fragment order
-            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int i = decltype(ic)::value;
-                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                    constexpr int j = decltype(jc)::value;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), rW,
-                                                           base + (i * SN + j) * 64 * 16, s * PART * 4,
-                                                           CPOL_COHERENT);
-                });
-            });
+            publish_partial(acc, rW, base, PART * 4, s);
             __builtin_amdgcn_s_waitcnt(0);                  // partial stores complete before the count
             __syncthreads();
             if (tid == 0)
@@ -401,36 +393,7 @@ pipe_kernel(PipeParams p) {
                                                  __HIP_MEMORY_SCOPE_AGENT) == S - 1;
             __syncthreads();
             if (!is_last) return;
-            v4f sum[SM][SN];
-            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                    sum[decltype(ic)::value][decltype(jc)::value] = v4f{0.f, 0.f, 0.f, 0.f};
-                });
-            });
-            for (int s2 = 0; s2 < S; ++s2) {
-                v4f part[SM][SN];
-                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                    constexpr int i = decltype(ic)::value;
-                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                        constexpr int j = decltype(jc)::value;
-                        part[i][j] = __builtin_bit_cast(
-                            v4f, __builtin_amdgcn_raw_buffer_load_b128(rW, base + (i * SN + j) * 64 * 16,
-                                                                       s2 * PART * 4, CPOL_COHERENT));
-                    });
-                });
-                static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                    constexpr int i = decltype(ic)::value;
-                    static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                        constexpr int j = decltype(jc)::value;
-                        sum[i][j] += s2 == s ? acc[i][j] : part[i][j];
-                    });
-                });
-            }
-            static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                    acc[decltype(ic)::value][decltype(jc)::value] = sum[decltype(ic)::value][decltype(jc)::value];
-                });
-            });
+            sum_partials(acc, rW, base, PART * 4, S, s);
             if (tid == 0) __hip_atomic_store(p.counters + t_all, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -446,15 +409,18 @@ pipe_kernel(PipeParams p) {
     constexpr int SEG = TN / 8;                  // 8-column segments per row
     constexpr int NQ = EPI_ROWS * SEG / 64;      // items per lane per chunk
     constexpr int NCH = TM / EPI_ROWS;
-    static_assert(TM <= 64 && (EPI_ROWS * SEG) % 64 == 0, "row mask and item split");
-    // rows of the wave's tile that are stored, one bit each
-    uint64_t rows_ok;
-    {
-        const int r = row0 + lane;
-        bool ok = lane < TM && r < valid_m;
+    static_assert(64 % EPI_ROWS == 0 && (EPI_ROWS * SEG) % 64 == 0, "row masks and item split");
+    // rows of the wave's tile that are stored, one bit each, 64 rows per mask
+    // (a chunk's rows share one mask)
+    constexpr int NRM = (TM + 63) / 64;
+    uint64_t rows_ok[NRM];
+    static_for<NRM>([&](auto hc) __attribute__((always_inline)) {
+        constexpr int h = decltype(hc)::value;
+        const int r = row0 + 64 * h + lane;
+        bool ok = 64 * h + lane < TM && r < valid_m;
         if (MODE == Mode::Contig) ok = ok && p.idx[r] >= 0;
-        rows_ok = __ballot(ok);
-    }
+        rows_ok[h] = __ballot(ok);
+    });
     const bool vec = (N % 8) == 0;
     v4i cr[NCH][NQ];
     static_for<NCH>([&](auto cc) __attribute__((always_inline)) {
@@ -464,7 +430,7 @@ pipe_kernel(PipeParams p) {
             const int r = c * EPI_ROWS + item / SEG;
             const int col = col0 + (item % SEG) * 8;
             cr[c][q] = v4i{0, 0, 0, 0};
-            if (C && vec && ((rows_ok >> r) & 1) && col < N)
+            if (C && vec && ((rows_ok[c * EPI_ROWS / 64] >> (r & 63)) & 1) && col < N)
                 cr[c][q] = *reinterpret_cast<const v4i *>(C + (int64_t)(row0 + r) * N + col);
         });
     });
@@ -475,9 +441,8 @@ pipe_kernel(PipeParams p) {
             constexpr int i = c * (EPI_ROWS / 16) + ii;
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
-                const v4f a4 = acc[i][j];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) stage[(ii * 16 + 4 * g4 + v) * EPI_PITCH + j * 16 + l16] = a4[v];
+                // row 16i + l%16, columns 16j + 4(l/16) .. +3
+                *reinterpret_cast<v4f *>(stage + (ii * 16 + l16) * EPI_PITCH + j * 16 + 4 * g4) = acc[i][j];
             });
         });
         static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
@@ -487,7 +452,7 @@ pipe_kernel(PipeParams p) {
             const int r = c * EPI_ROWS + rl;
             const int row = row0 + r;
             const int col = col0 + sgi * 8;
-            if (((rows_ok >> r) & 1) && col < N) {
+            if (((rows_ok[c * EPI_ROWS / 64] >> (r & 63)) & 1) && col < N) {
                 const float *sp = stage + rl * EPI_PITCH + sgi * 8;
                 const v4f lo = *reinterpret_cast<const v4f *>(sp);
                 const v4f hi = *reinterpret_cast<const v4f *>(sp + 4);
@@ -611,13 +576,17 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
             }
             return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true>(p, cus, stream, config);
         }
-        // prefill shapes.  Short K (few blocks per tile): 128x128 tiles on 8
-        // waves with two stages leave room for two workgroups per CU, so one
-        // workgroup's epilogue and pipeline fill overlap the other's MFMAs.
-        // Long K: 256x128 tiles with three stages (measured on MI355X for
-        // M = 4096 and (N, K) in {(4096, 7168), (7168, 2048), (24576, 1536)}).
-        if (nkb <= 16) return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
-        return launch_pipe_t<256, 128, 4, 2, 3, 1, true, Mode::Dense, false>(p, 0, stream, config);
+        // prefill shapes.  256x256 tiles (8 waves of 128x64, two stages) read
+        // the fewest bytes from LDS and from L2 per MFMA.  With short K (few
+        // blocks per tile) and a last wave of tiles that leaves CUs idle,
+        // 128x128 tiles with two workgroups per CU do better: one
+        // workgroup's epilogue and pipeline fill overlap the other's MFMAs
+        // (measured on MI355X for M = 4096 and (N, K) in {(4096, 7168),
+        // (7168, 2048), (24576, 1536)}).
+        const int64_t t256 = (int64_t)((p.rows_a + 255) / 256) * ((p.N + 255) / 256);
+        if (p.rows_a >= 256 && (nkb > 16 || t256 % cus == 0))
+            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
+        return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
     }
     case Mode::Contig:   // expert segments are 128-row aligned: one expert per 128-row tile
         return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false>(p, 0, stream, config);

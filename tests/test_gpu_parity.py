@@ -123,7 +123,7 @@ def test_dense_small_config_full_compare():
 
 @pytest.mark.parametrize("M,N,K,with_c", [(1, 2112, 256, False), (37, 200, 384, True), (129, 129, 128, True),
                                           (257, 300, 512, False), (64, 2112, 7168, False),
-                                          (200, 1000, 1024, True), (5, 16, 128, True)])
+                                          (200, 1000, 1024, True), (5, 16, 128, True), (520, 600, 2304, True)])
 def test_dense_shapes_and_tails_full_compare(M, N, K, with_c):
     announce(f"dense M={M} N={N} K={K} C={with_c}")
     p = dense_problem(M, N, K, seed=M * 7 + N, with_c=with_c)
@@ -132,12 +132,13 @@ def test_dense_shapes_and_tails_full_compare(M, N, K, with_c):
     check_close(got, ref, f"dense {M}x{N}x{K}")
 
 
-def test_dense_identity_power_of_two_scales_bitexact():
+@pytest.mark.parametrize("M,K", [(96, 512), (300, 2304)])
+def test_dense_identity_power_of_two_scales_bitexact(M, K):
     """B = identity, power-of-two scales: each D[m,n] is one exactly
     representable product, so GPU and oracle agree bit for bit.  This pins
     the operand lane layout, the transposed sfa index, the per-block sfb index
-    and the row/column mapping of the output."""
-    M, K = 96, 512
+    and the row/column mapping of the output, for a decode-shaped (split-K)
+    and a prefill-shaped launch."""
     N = K
     announce(f"dense identity M={M} N=K={K}")
     a = synth.random_codes(3, 0, (M, K))
