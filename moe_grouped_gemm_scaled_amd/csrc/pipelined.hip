@@ -62,6 +62,55 @@ struct PipeParams {
     int splits_lo, split_hi, slots;
 };
 
+// Contiguous layout with 256-row tiles: the u-th "unit" of 256 rows.  Units
+// start at every other 128-row block of an expert's segment (its first
+// block, its third, ...), so a unit never mixes two experts' rows; the last
+// unit of a segment with an odd number of blocks holds 128 of them (its
+// other rows are not stored).  Every lane of the wave gets the unit's first
+// block, or -1 if there are fewer units.  The segments are read from the
+// expert index of each block's first row (segments are 128-row aligned),
+// four blocks per lane at a time, all loads in flight together.
+__device__ __forceinline__ int contig_unit_block(const int32_t *idx, int nblocks, int u) {
+    const int lane = threadIdx.x & 63;
+    int prev_e = -1;     // expert of the block before this round (none: -1)
+    int seg = -1;        // first block of the segment running into this round
+    int count = 0;       // units before this round
+    for (int base = 0; base < nblocks; base += 256) {
+        int e[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int b = base + 64 * q + lane;
+            e[q] = b < nblocks ? idx[(int64_t)b * 128] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int b = base + 64 * q + lane;
+            int ep = __shfl_up(e[q], 1);
+            if (lane == 0) ep = prev_e;
+            const bool start = e[q] >= 0 && e[q] != ep;
+            int sg = start ? b : -1;                  // inclusive max-scan of segment starts
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(sg, o);
+                if (lane >= o) sg = sg > t ? sg : t;
+            }
+            sg = sg > seg ? sg : seg;
+            const bool unit = e[q] >= 0 && ((b - sg) & 1) == 0;
+            const uint64_t m = __ballot(unit);
+            const int n = __popcll(m);
+            if (u < count + n) {
+                const int rank = __popcll(m & ((1ull << lane) - 1ull));
+                const uint64_t hit = __ballot(unit && rank == u - count);
+                return base + 64 * q + __ffsll((unsigned long long)hit) - 1;
+            }
+            count += n;
+            prev_e = __shfl(e[q], 63);
+            seg = __shfl(sg, 63);
+        }
+    }
+    return -1;
+}
+
 template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 pipe_kernel(PipeParams p) {
@@ -148,7 +197,12 @@ pipe_kernel(PipeParams p) {
     } else {
         raster(t_lin, p.tiles_m, p.tiles_n, p.gm, tm, tn);
     }
-    const int m0 = tm * BM;
+    int m0 = tm * BM;
+    if constexpr (MODE == Mode::Contig && BM == 256) {
+        const int ub = __builtin_amdgcn_readfirstlane(contig_unit_block(p.idx, p.rows_a / 128, tm));
+        if (ub < 0) return;                        // no such unit: uniform exit
+        m0 = ub * 128;
+    }
     const int n0 = tn * BN;
     // K range of this workgroup, in steps of KS blocks (nkb is a multiple of KS)
     const int nsteps_all = nkb / KS;
@@ -176,11 +230,13 @@ pipe_kernel(PipeParams p) {
         SFB += (int64_t)grp * nnb * nkb;
         if (C) C += (int64_t)grp * rows_a * N;
         D += (int64_t)grp * rows_a * N;
-    } else if (MODE == Mode::Contig) {
-        const int e = p.idx[m0];
-        if (e < 0) return;                         // tile of padding rows: uniform exit
-        B += (int64_t)e * N * K;
-        SFB += (int64_t)e * nnb * nkb;
+    }
+    int expert = 0;                                // contiguous: the tile's expert; its rows are the ones stored
+    if (MODE == Mode::Contig) {
+        expert = p.idx[m0];
+        if (expert < 0) return;                    // tile of padding rows: uniform exit
+        B += (int64_t)expert * N * K;
+        SFB += (int64_t)expert * nnb * nkb;
     }
 
     const int tid = threadIdx.x;
@@ -418,7 +474,7 @@ pipe_kernel(PipeParams p) {
         constexpr int h = decltype(hc)::value;
         const int r = row0 + 64 * h + lane;
         bool ok = 64 * h + lane < TM && r < valid_m;
-        if (MODE == Mode::Contig) ok = ok && p.idx[r] >= 0;
+        if (MODE == Mode::Contig) ok = ok && p.idx[r] == expert;
         rows_ok[h] = __ballot(ok);
     });
     const bool vec = (N % 8) == 0;
@@ -501,6 +557,11 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
     k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.d = p.d; k.idx = p.idx;
     k.rows_a = p.rows_a; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.G = p.G;
     k.tiles_m = (p.rows_a + BM - 1) / BM;
+    if (MODE == Mode::Contig && BM == 256) {
+        // units: at most one per 256 rows plus one per expert segment
+        if (p.rows_a % 128 != 0) return hipErrorInvalidValue;
+        k.tiles_m = p.rows_a / 256 + p.G + 1;
+    }
     k.tiles_n = (p.N + BN - 1) / BN;
     k.gm = 4;
     k.ws = nullptr;
@@ -588,7 +649,12 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
             return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
         return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
     }
-    case Mode::Contig:   // expert segments are 128-row aligned: one expert per 128-row tile
+    case Mode::Contig:
+        // 256-row units that never mix experts (the segments are 128-row
+        // aligned); measured on MI355X for 8 experts, N = 4096, K = 7168:
+        // 540 us against 575 us with 128x256 tiles
+        if (p.rows_a >= 256)
+            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Contig, false>(p, 0, stream, config);
         return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false>(p, 0, stream, config);
     case Mode::Masked:
         return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false>(p, 0, stream, config);

@@ -219,6 +219,28 @@ def test_contiguous_edge_counts():
         check_close(dense, ref[rows], f"dense on expert {g}")
 
 
+
+def test_contiguous_many_experts():
+    """More than 256 aligned 128-row blocks and many segments of one, two and
+    three blocks, with empty experts between them: the unit scan of the
+    256-row-tile path runs over several rounds, and units must neither mix
+    experts nor skip any."""
+    counts = [0 if g % 7 == 3 else int(c) for g, c in enumerate(synth.randint(31, 3, 300, 0, 300))]
+    N, K = 136, 256
+    announce(f"contiguous many experts G={len(counts)} rows={sum(counts)}")
+    p = contiguous_problem(counts, N, K, seed=31, with_c=True)
+    assert p["M_total"] // 128 > 256
+    out = Guarded((p["M_total"], N))
+    dg.m_grouped_fp8_gemm_nt_contiguous(dev(p["a"]), dev(p["sfa"]), dev(p["b"]), dev(p["sfb"]), out.t,
+                                        dev(p["m_indices"]), c=dev_bf16(p["c"]))
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    got = out.bits()
+    ref = oracle.m_grouped_contiguous(p["a"], p["sfa"], p["b"], p["sfb"], p["c"], p["m_indices"])
+    valid = p["m_indices"] >= 0
+    check_close(got[valid], ref[valid], f"contiguous many experts ({dg.last_config()})")
+    assert np.all(got[~valid] == SENTINEL)
+
 # ---------------------------------------------------------------- full-size workloads (sampled)
 
 
