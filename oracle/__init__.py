@@ -37,6 +37,9 @@ def _load():
         "orc_block_scale": (_ct.c_float, [_ct.c_float]),
         "orc_quantize_1x128": (None, [P, I, I, I, P, P, I]),
         "orc_quantize_128x128": (None, [P, I, I, I, P, P]),
+        "orc_block_scale_ue8m0": (_ct.c_float, [_ct.c_float]),
+        "orc_quantize_1x128_ue8m0": (None, [P, I, I, I, P, P, I]),
+        "orc_quantize_128x128_ue8m0": (None, [P, I, I, I, P, P]),
         "orc_bf16_to_double": (D, [_ct.c_uint16]),
         "orc_gemm_nt_elem": (D, [P, P, I, P, P, P, I, I, I, I, I]),
         "orc_gemm_nt": (None, [P, P, I, P, P, P, P, I, I, I]),
@@ -86,8 +89,13 @@ def sf_aligned(mn):
     return (mn + 3) // 4 * 4
 
 
-def quantize_1x128(x, ld_sf=None):
-    """x[groups, rows, K] (or [rows, K]) fp32 -> (q uint8 same shape, sf[groups, K/128, ld_sf])."""
+def block_scale_ue8m0(amax):
+    return _np.float32(_load().orc_block_scale_ue8m0(float(amax)))
+
+
+def quantize_1x128(x, ld_sf=None, ue8m0=False):
+    """x[groups, rows, K] (or [rows, K]) fp32 -> (q uint8 same shape, sf[groups, K/128, ld_sf]).
+    ue8m0: power-of-two scales (the block scale rounded up to a power of two)."""
     x = _np.ascontiguousarray(x, dtype=_np.float32)
     squeeze = x.ndim == 2
     x3 = x[None] if squeeze else x
@@ -96,14 +104,16 @@ def quantize_1x128(x, ld_sf=None):
     ld = sf_aligned(rows) if ld_sf is None else ld_sf
     q = _np.empty(x3.shape, dtype=_np.uint8)
     sf = _np.zeros((groups, K // 128, ld), dtype=_np.float32)
-    _load().orc_quantize_1x128(x3.ctypes.data, groups, rows, K, q.ctypes.data, sf.ctypes.data, ld)
+    f = _load().orc_quantize_1x128_ue8m0 if ue8m0 else _load().orc_quantize_1x128
+    f(x3.ctypes.data, groups, rows, K, q.ctypes.data, sf.ctypes.data, ld)
     if squeeze:
         return q[0], sf[0]
     return q, sf
 
 
-def quantize_128x128(x):
-    """x[groups, rows, K] (or [rows, K]) -> (q, sf[groups, ceil(rows/128), K/128])."""
+def quantize_128x128(x, ue8m0=False):
+    """x[groups, rows, K] (or [rows, K]) -> (q, sf[groups, ceil(rows/128), K/128]).
+    ue8m0: power-of-two scales."""
     x = _np.ascontiguousarray(x, dtype=_np.float32)
     squeeze = x.ndim == 2
     x3 = x[None] if squeeze else x
@@ -111,7 +121,8 @@ def quantize_128x128(x):
     assert K % 128 == 0
     q = _np.empty(x3.shape, dtype=_np.uint8)
     sf = _np.empty((groups, (rows + 127) // 128, K // 128), dtype=_np.float32)
-    _load().orc_quantize_128x128(x3.ctypes.data, groups, rows, K, q.ctypes.data, sf.ctypes.data)
+    f = _load().orc_quantize_128x128_ue8m0 if ue8m0 else _load().orc_quantize_128x128
+    f(x3.ctypes.data, groups, rows, K, q.ctypes.data, sf.ctypes.data)
     if squeeze:
         return q[0], sf[0]
     return q, sf

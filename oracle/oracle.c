@@ -112,8 +112,27 @@ float orc_block_scale(float amax)
     return a / 448.0f;
 }
 
-void orc_quantize_1x128(const float *x, int groups, int rows, int K,
-                        uint8_t *q, float *sf, int ld_sf)
+/* Power-of-two (UE8M0) variant of the block scale, the form the DeepGEMM
+ * README summary describes for its SM100 kernels ("packed UE8M0" scaling
+ * factors): the fp32 quotient above rounded up to the next power of two, so
+ * that every |x / s| still fits E4M3 (s >= amax/448) and s is as small as
+ * such a power allows.  frexp gives s = m * 2^e with m in [0.5, 1); s is a
+ * power of two exactly when m == 0.5. */
+float orc_block_scale_ue8m0(float amax)
+{
+    const float s = orc_block_scale(amax);
+    int e;
+    const float m = frexpf(s, &e);
+    return m == 0.5f ? s : ldexpf(1.0f, e);
+}
+
+static float block_scale_mode(float amax, int ue8m0)
+{
+    return ue8m0 ? orc_block_scale_ue8m0(amax) : orc_block_scale(amax);
+}
+
+static void quantize_1x128_mode(const float *x, int groups, int rows, int K,
+                                uint8_t *q, float *sf, int ld_sf, int ue8m0)
 {
     table_init();
     const int nkb = K / 128;
@@ -128,15 +147,27 @@ void orc_quantize_1x128(const float *x, int groups, int rows, int K,
                     if (v > amax)
                         amax = v;
                 }
-                const float s = orc_block_scale(amax);
+                const float s = block_scale_mode(amax, ue8m0);
                 for (int k = 0; k < 128; ++k)
                     q[base + k] = orc_e4m3_encode(x[base + k] / s);
                 sf[((size_t)g * nkb + kb) * (size_t)ld_sf + r] = s;
             }
 }
 
-void orc_quantize_128x128(const float *x, int groups, int rows, int K,
-                          uint8_t *q, float *sf)
+void orc_quantize_1x128(const float *x, int groups, int rows, int K,
+                        uint8_t *q, float *sf, int ld_sf)
+{
+    quantize_1x128_mode(x, groups, rows, K, q, sf, ld_sf, 0);
+}
+
+void orc_quantize_1x128_ue8m0(const float *x, int groups, int rows, int K,
+                              uint8_t *q, float *sf, int ld_sf)
+{
+    quantize_1x128_mode(x, groups, rows, K, q, sf, ld_sf, 1);
+}
+
+static void quantize_128x128_mode(const float *x, int groups, int rows, int K,
+                                  uint8_t *q, float *sf, int ue8m0)
 {
     table_init();
     const int nkb = K / 128;
@@ -154,7 +185,7 @@ void orc_quantize_128x128(const float *x, int groups, int rows, int K,
                         if (v > amax)
                             amax = v;
                     }
-                const float s = orc_block_scale(amax);
+                const float s = block_scale_mode(amax, ue8m0);
                 for (int r = r0; r < r1; ++r)
                     for (int k = 0; k < 128; ++k) {
                         const size_t i = ((size_t)g * rows + r) * (size_t)K + (size_t)kb * 128 + k;
@@ -162,6 +193,18 @@ void orc_quantize_128x128(const float *x, int groups, int rows, int K,
                     }
                 sf[((size_t)g * nrb + rb) * (size_t)nkb + kb] = s;
             }
+}
+
+void orc_quantize_128x128(const float *x, int groups, int rows, int K,
+                          uint8_t *q, float *sf)
+{
+    quantize_128x128_mode(x, groups, rows, K, q, sf, 0);
+}
+
+void orc_quantize_128x128_ue8m0(const float *x, int groups, int rows, int K,
+                                uint8_t *q, float *sf)
+{
+    quantize_128x128_mode(x, groups, rows, K, q, sf, 1);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -65,6 +65,16 @@ void orc_quantize_1x128(const float *x, int groups, int rows, int K,
 void orc_quantize_128x128(const float *x, int groups, int rows, int K,
                           uint8_t *q, float *sf);
 
+/* Power-of-two (UE8M0) scale variants: the block scale is orc_block_scale(amax)
+ * rounded up to the next power of two (orc_block_scale_ue8m0), otherwise as
+ * above.  Dividing by a power of two is exact, so the codes are the E4M3
+ * rounding of x * 2^-e. */
+float orc_block_scale_ue8m0(float amax);
+void orc_quantize_1x128_ue8m0(const float *x, int groups, int rows, int K,
+                              uint8_t *q, float *sf, int ld_sf);
+void orc_quantize_128x128_ue8m0(const float *x, int groups, int rows, int K,
+                                uint8_t *q, float *sf);
+
 /* bf16 bit pattern -> fp64 (exact). */
 double orc_bf16_to_double(uint16_t h);
 

@@ -236,6 +236,69 @@ def test_quantize_groups_do_not_share_blocks_and_ld_padding_untouched():
         assert np.array_equal(q1[g], qg) and np.array_equal(sf1[g][:, :130], sfg[:, :130])
 
 
+@pytest.mark.parametrize("kind", ["1x128", "128x128"])
+def test_quantize_ue8m0_scales_are_minimal_powers_of_two(kind):
+    """Power-of-two scale variant: every scale is a power of two, at least
+    the block's amax/448 (so nothing saturates) and less than twice it (the
+    smallest such power).  Data spans many binades, including blocks whose
+    amax/448 is itself a power of two and an all-zero block."""
+    x = synth.normal_f32(23, 0, (260, 512)) * np.ldexp(np.float32(1.0), synth.randint(23, 1, 260 * 512, -20, 20).reshape(260, 512)).astype(np.float32)
+    x[5, :128] = 0.0
+    x[6, :128] = 0.0
+    x[6, 7] = -448.0 * 2.0 ** -5
+    if kind == "1x128":
+        q, sf = oracle.quantize_1x128(x, ue8m0=True)
+        amax = np.abs(x).reshape(260, 4, 128).max(axis=2).T            # [K/128, rows]
+        sf = sf[:, :260]
+    else:
+        q, sf = oracle.quantize_128x128(x, ue8m0=True)
+        amax = np.array([[np.abs(x[rb * 128:(rb + 1) * 128, kb * 128:(kb + 1) * 128]).max() for kb in range(4)]
+                         for rb in range(3)])
+    quot = np.maximum(amax, np.float32(1e-4)).astype(np.float32) / np.float32(448.0)
+    mant, _ = np.frexp(sf)
+    assert np.all(mant == 0.5)                       # powers of two
+    assert np.all(sf >= quot) and np.all(sf / 2 < quot)
+    if kind == "1x128":
+        assert sf[0, 6] == np.float32(2.0 ** -5)    # amax/448 already a power of two: kept
+        assert sf[0, 5] == np.float32(2.0 ** -22)   # zero block: 1e-4/448 rounded up
+
+
+@pytest.mark.parametrize("kind", ["1x128", "128x128"])
+def test_quantize_ue8m0_codes_are_the_e4m3_rounding_of_x_times_two_to_minus_e(kind):
+    """Dividing by a power of two is exact, so the codes must equal torch's
+    own E4M3 cast of x * 2^-e (an encoder that shares nothing with the
+    oracle's), with no saturation."""
+    x = synth.normal_f32(24, 0, (200, 384)) * np.float32(3.0)
+    if kind == "1x128":
+        q, sf = oracle.quantize_1x128(x, ue8m0=True)
+        s_full = np.repeat(sf[:, :200].T, 128, axis=1)
+    else:
+        q, sf = oracle.quantize_128x128(x, ue8m0=True)
+        s_full = np.repeat(np.repeat(sf, 128, axis=0)[:200], 128, axis=1)
+    _, e = np.frexp(s_full)
+    y = np.ldexp(x, 1 - e).astype(np.float32)       # x / s exactly (s = 2^(e-1))
+    assert np.all(np.abs(y) <= 448.0)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+
+
+def test_quantize_ue8m0_equals_plain_when_scales_are_powers_of_two():
+    """Blocks whose amax is 448 times a power of two have a power-of-two
+    plain scale already: both quantisers give the same codes and scales."""
+    x = synth.normal_f32(25, 0, (64, 256))
+    for r in range(64):
+        for kb in range(2):
+            blk = x[r, kb * 128:(kb + 1) * 128]
+            top = np.float32(448.0 * 2.0 ** ((r + kb) % 9 - 4))
+            i = np.argmax(np.abs(blk))
+            blk *= top / np.abs(blk[i])
+            np.clip(blk, -top, top, out=blk)
+            blk[i] = top if blk[i] > 0 else -top       # amax exactly 448 * 2^k
+    q0, s0 = oracle.quantize_1x128(x)
+    q1, s1 = oracle.quantize_1x128(x, ue8m0=True)
+    assert np.array_equal(q0, q1) and np.array_equal(s0, s1)
+
+
 # ---------------------------------------------------------------- GEMM
 
 
