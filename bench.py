@@ -1,6 +1,7 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|contiguous|masked|small]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload decode|prefill|contiguous|masked|small|prefill_ue8m0|contiguous_ue8m0]
 
 A step is one pass of the hot path over one batch of synthetic input: for
 every GEMM of the workload, quantise the fp32 activations (1x128 scales) and
@@ -89,9 +90,9 @@ def n_copies(weight_bytes):
     return max(2, cdiv(ROTATE_BYTES, max(1, weight_bytes)) + 1)
 
 
-def make_weights(G, N, K, seed):
+def make_weights(G, N, K, seed, ue8m0=False):
     xb = torch.from_numpy(synth.normal_f32(seed, synth.STREAM_B, (G, N, K))).cuda()
-    b, sfb = dg.quantize_e4m3_128x128(xb)
+    b, sfb = dg.quantize_e4m3_128x128(xb, ue8m0=ue8m0)
     del xb
     return b, sfb
 
@@ -100,14 +101,14 @@ def replicate(t, n):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
-def dense_jobs(cfgs):
+def dense_jobs(cfgs, ue8m0=False):
     jobs = []
     weights = {}
     for cfg in cfgs:
         M, N, K, seed = cfg["M"], cfg["N"], cfg["K"], cfg["seed"]
         key = (M, N, K)           # no sharing between jobs: every GEMM streams its own copies
         if key not in weights:
-            b, sfb = make_weights(1, N, K, seed)
+            b, sfb = make_weights(1, N, K, seed, ue8m0)
             nc = n_copies(N * K)
             weights[key] = (replicate(b[0], nc), replicate(sfb[0], nc))
         bs, sfbs = weights[key]
@@ -122,20 +123,20 @@ def dense_jobs(cfgs):
 
         def launch(ci, with_quant, x=x, a=a, sfa=sfa, bs=bs, sfbs=sfbs, c=c, d=d):
             if with_quant:
-                dg.quantize_e4m3_1x128(x, q=a, sf=sfa)
-            dg.fp8_gemm_nt(a, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c)
+                dg.quantize_e4m3_1x128(x, q=a, sf=sfa, ue8m0=ue8m0)
+            dg.fp8_gemm_nt(a, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c, ue8m0=ue8m0)
 
         jobs.append(Job(cfg["name"], launch, len(bs), 2.0 * M * N * K,
                         gemm_bytes(M, N, K, with_c=cfg["with_c"]), quant_bytes(M, K)))
     return jobs
 
 
-def contiguous_jobs():
+def contiguous_jobs(ue8m0=False):
     cfg = synth.CONTIGUOUS
     counts = synth.contiguous_counts(cfg)
     m_idx = synth.contiguous_m_indices(counts)
     M_total, N, K, G = m_idx.size, cfg["N"], cfg["K"], cfg["G"]
-    b, sfb = make_weights(G, N, K, cfg["seed"])
+    b, sfb = make_weights(G, N, K, cfg["seed"], ue8m0)
     nc = n_copies(G * N * K)
     bs, sfbs = replicate(b, nc), replicate(sfb, nc)
     x = torch.from_numpy(synth.normal_f32(cfg["seed"], synth.STREAM_A, (M_total, K))).cuda()
@@ -147,8 +148,8 @@ def contiguous_jobs():
 
     def launch(ci, with_quant):
         if with_quant:
-            dg.quantize_e4m3_1x128(x, q=a, sf=sfa)
-        dg.m_grouped_fp8_gemm_nt_contiguous(a, sfa, bs[ci % nc], sfbs[ci % nc], d, mi)
+            dg.quantize_e4m3_1x128(x, q=a, sf=sfa, ue8m0=ue8m0)
+        dg.m_grouped_fp8_gemm_nt_contiguous(a, sfa, bs[ci % nc], sfbs[ci % nc], d, mi, ue8m0=ue8m0)
 
     return [Job(cfg["name"], launch, nc, 2.0 * m_valid * N * K, gemm_bytes(m_valid, N, K, G),
                 quant_bytes(M_total, K))], dict(counts=counts.tolist(), M_total=M_total, m_valid=m_valid)
@@ -307,7 +308,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "contiguous", "masked", "small"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "contiguous", "masked", "small", "prefill_ue8m0", "contiguous_ue8m0"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB each (reference for HBM byte counters)")
@@ -336,6 +338,12 @@ def main():
         bound = "hbm"
     elif args.workload == "prefill":
         jobs = dense_jobs(synth.PREFILL)
+        bound = "mfma"
+    elif args.workload == "prefill_ue8m0":
+        jobs = dense_jobs(synth.PREFILL, ue8m0=True)
+        bound = "mfma"
+    elif args.workload == "contiguous_ue8m0":
+        jobs, meta = contiguous_jobs(ue8m0=True)
         bound = "mfma"
     elif args.workload == "small":
         jobs = dense_jobs([synth.DENSE_SMALL])
@@ -408,6 +416,10 @@ def main():
         "contiguous": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168",
         "masked": "M-grouped masked FP8 GEMM, 16 experts x 256 rows, masked_m U[0,256], N=7168, K=2048",
         "small": "dense FP8 NT GEMM M=128, N=256, K=512",
+        "prefill_ue8m0": "prefill-shaped dense FP8 NT GEMM, M=4096 x (N,K) in {(4096,7168),(7168,2048),(24576,1536)}, "
+                         "C bf16, bf16 D, power-of-two (UE8M0) block scales",
+        "contiguous_ue8m0": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168, "
+                            "power-of-two (UE8M0) block scales",
     }[args.workload]
     out = {
         "metric": METRIC,
@@ -421,7 +433,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3",
-        "data": "synthetic: seeded N(0,1) fp32, quantised to e4m3 with 1x128 / 128x128 fp32 scales",
+        "data": "synthetic: seeded N(0,1) fp32, quantised to e4m3 with 1x128 / 128x128 fp32 scales"
+                + (" rounded up to powers of two (UE8M0)" if args.workload.endswith("_ue8m0") else ""),
         "config": {"workload": workload_desc, "step": "activation quantiser + GEMM per shape; weights pre-quantised",
                    "graph_replay": True, **({"layout": meta} if meta else {})},
         "roofline": roof,

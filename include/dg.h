@@ -135,6 +135,47 @@ int dg_quantize_e4m3_1x128(const float *x, int groups, int rows, int K,
 int dg_quantize_e4m3_128x128(const float *x, int groups, int rows, int K,
                              uint8_t *q, float *sf, void *stream);
 
+/*
+ * Power-of-two (UE8M0) scale variants.  The DeepGEMM README summary
+ * ("GEMM interface and layout constraints") describes packed UE8M0 scaling
+ * factors for its SM100 kernels: every scale a power of two.
+ *
+ * Quantisers: as above, but the block scale is max(amax, 1e-4)/448 (one
+ * IEEE fp32 division) rounded up to the next power of two, so |x/sf| <= 448
+ * still holds and the division is exact.  Same layouts and errors.
+ */
+int dg_quantize_e4m3_1x128_ue8m0(const float *x, int groups, int rows, int K,
+                                 uint8_t *q, float *sf, int ld_sf, void *stream);
+int dg_quantize_e4m3_128x128_ue8m0(const float *x, int groups, int rows, int K,
+                                   uint8_t *q, float *sf, void *stream);
+
+/*
+ * GEMMs on power-of-two scales: same arguments, layouts, results (to the
+ * same tolerance) and errors as the three GEMMs above, but every entry of
+ * sfa and sfb that scales a computed element must be a positive normal
+ * power of two, as the *_ue8m0 quantisers write them.  gfx950's FP8 matrix
+ * instruction then applies the scales itself, as exponents, and
+ * accumulates across K blocks without a separate promotion step.  The
+ * mantissa bits of a scale are not read: a scale that is not a power of
+ * two gives a wrong result (nothing checks this on the device).
+ */
+int dg_fp8_gemm_nt_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa,
+                         const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d,
+                         int M, int N, int K, void *stream);
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t *a, const float *sfa,
+                                              const uint8_t *b, const float *sfb,
+                                              const uint16_t *c, uint16_t *d,
+                                              const int32_t *m_indices,
+                                              int M_total, int N, int K, int G,
+                                              void *stream);
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t *a, const float *sfa,
+                                          const uint8_t *b, const float *sfb,
+                                          const uint16_t *c, uint16_t *d,
+                                          const int32_t *masked_m,
+                                          int G, int M_cap, int N, int K,
+                                          int expected_m, void *stream);
+
 /* Row alignment of expert segments in the contiguous layout (128).  The
  * setter accepts only 128 and returns DG_ERR_ARG otherwise. ("Utilities and
  * environment variables" section.) */

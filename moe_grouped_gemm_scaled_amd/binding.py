@@ -38,6 +38,18 @@ EXPORTS = {
                                           ct.c_int, ct.c_void_p]),
     "dg_quantize_e4m3_128x128": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p,
                                             ct.c_void_p]),
+    "dg_fp8_gemm_nt_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                        ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                             ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int,
+                                                             ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                         ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int,
+                                                         ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_quantize_e4m3_1x128_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
+                                                ct.c_void_p, ct.c_int, ct.c_void_p]),
+    "dg_quantize_e4m3_128x128_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
+                                                  ct.c_void_p, ct.c_void_p]),
     "dg_get_mk_alignment_for_contiguous_layout": (ct.c_int, []),
     "dg_set_mk_alignment_for_contiguous_layout": (ct.c_int, [ct.c_int]),
     "dg_get_sf_aligned_size": (ct.c_int, [ct.c_int]),
@@ -109,8 +121,13 @@ def ceil_div(a: int, b: int) -> int:
     return (a + b - 1) // b
 
 
-def fp8_gemm_nt(a, sfa, b, sfb, d, c=None):
-    """D = C + A . B^T.  a[M,K], sfa[K/128, ld_sfa], b[N,K], sfb[ceil(N/128), K/128], d/c[M,N] bf16."""
+def _name(base: str, ue8m0: bool) -> str:
+    return base + "_ue8m0" if ue8m0 else base
+
+
+def fp8_gemm_nt(a, sfa, b, sfb, d, c=None, ue8m0=False):
+    """D = C + A . B^T.  a[M,K], sfa[K/128, ld_sfa], b[N,K], sfb[ceil(N/128), K/128], d/c[M,N] bf16.
+    ue8m0: every scale is a power of two (dg_fp8_gemm_nt_ue8m0)."""
     M, K = a.shape
     N = b.shape[0]
     if sfa.dim() != 2 or sfa.shape[0] != K // 128:
@@ -118,11 +135,12 @@ def fp8_gemm_nt(a, sfa, b, sfb, d, c=None):
     args = (_ptr(a, _FP8, "a", (M, K)), _ptr(sfa, torch.float32, "sfa"), int(sfa.shape[1]),
             _ptr(b, _FP8, "b", (N, K)), _ptr(sfb, torch.float32, "sfb", (ceil_div(N, 128), K // 128)),
             _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
-    _check(lib().dg_fp8_gemm_nt(*args), "dg_fp8_gemm_nt")
+    name = _name("dg_fp8_gemm_nt", ue8m0)
+    _check(getattr(lib(), name)(*args), name)
     return d
 
 
-def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, m_indices, c=None):
+def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, m_indices, c=None, ue8m0=False):
     """a[M_total,K], sfa[K/128, M_total], b[G,N,K], sfb[G, ceil(N/128), K/128], d/c[M_total,N], m_indices[M_total]."""
     M_total, K = a.shape
     G, N, _ = b.shape
@@ -130,11 +148,12 @@ def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, m_indices, c=None):
             _ptr(b, _FP8, "b", (G, N, K)), _ptr(sfb, torch.float32, "sfb", (G, ceil_div(N, 128), K // 128)),
             _ptr(c, torch.bfloat16, "c", (M_total, N)), _ptr(d, torch.bfloat16, "d", (M_total, N)),
             _ptr(m_indices, torch.int32, "m_indices", (M_total,)), M_total, N, K, G, _stream(d))
-    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous(*args), "dg_m_grouped_fp8_gemm_nt_contiguous")
+    name = _name("dg_m_grouped_fp8_gemm_nt_contiguous", ue8m0)
+    _check(getattr(lib(), name)(*args), name)
     return d
 
 
-def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, c=None):
+def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, c=None, ue8m0=False):
     """a[G,M_cap,K], sfa[G, K/128, round_up(M_cap,4)], b[G,N,K], sfb[G, ceil(N/128), K/128], d/c[G,M_cap,N]."""
     G, M_cap, K = a.shape
     N = b.shape[1]
@@ -143,12 +162,14 @@ def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, c=No
             _ptr(b, _FP8, "b", (G, N, K)), _ptr(sfb, torch.float32, "sfb", (G, ceil_div(N, 128), K // 128)),
             _ptr(c, torch.bfloat16, "c", (G, M_cap, N)), _ptr(d, torch.bfloat16, "d", (G, M_cap, N)),
             _ptr(masked_m, torch.int32, "masked_m", (G,)), G, M_cap, N, K, int(expected_m), _stream(d))
-    _check(lib().dg_m_grouped_fp8_gemm_nt_masked(*args), "dg_m_grouped_fp8_gemm_nt_masked")
+    name = _name("dg_m_grouped_fp8_gemm_nt_masked", ue8m0)
+    _check(getattr(lib(), name)(*args), name)
     return d
 
 
-def quantize_e4m3_1x128(x, q=None, sf=None, ld_sf=None):
-    """x[groups, rows, K] or [rows, K] fp32 -> (q uint8, sf[groups, K/128, ld_sf] or [K/128, ld_sf])."""
+def quantize_e4m3_1x128(x, q=None, sf=None, ld_sf=None, ue8m0=False):
+    """x[groups, rows, K] or [rows, K] fp32 -> (q uint8, sf[groups, K/128, ld_sf] or [K/128, ld_sf]).
+    ue8m0: power-of-two scales (dg_quantize_e4m3_1x128_ue8m0)."""
     squeeze = x.dim() == 2
     groups, rows, K = (1,) + tuple(x.shape) if squeeze else tuple(x.shape)
     ld = (rows + 3) // 4 * 4 if ld_sf is None else int(ld_sf)
@@ -159,12 +180,14 @@ def quantize_e4m3_1x128(x, q=None, sf=None, ld_sf=None):
     _ptr(sf, torch.float32, "sf", (K // 128, ld) if squeeze else (groups, K // 128, ld))
     args = (_ptr(x, torch.float32, "x"), groups, rows, K, _ptr(q, _FP8, "q", tuple(x.shape)),
             ct.c_void_p(sf.data_ptr()), ld, _stream(x))
-    _check(lib().dg_quantize_e4m3_1x128(*args), "dg_quantize_e4m3_1x128")
+    name = _name("dg_quantize_e4m3_1x128", ue8m0)
+    _check(getattr(lib(), name)(*args), name)
     return q, sf
 
 
-def quantize_e4m3_128x128(x, q=None, sf=None):
-    """x[groups, rows, K] or [rows, K] fp32 -> (q uint8, sf[groups, ceil(rows/128), K/128])."""
+def quantize_e4m3_128x128(x, q=None, sf=None, ue8m0=False):
+    """x[groups, rows, K] or [rows, K] fp32 -> (q uint8, sf[groups, ceil(rows/128), K/128]).
+    ue8m0: power-of-two scales (dg_quantize_e4m3_128x128_ue8m0)."""
     squeeze = x.dim() == 2
     groups, rows, K = (1,) + tuple(x.shape) if squeeze else tuple(x.shape)
     shape_sf = (ceil_div(rows, 128), K // 128) if squeeze else (groups, ceil_div(rows, 128), K // 128)
@@ -174,7 +197,8 @@ def quantize_e4m3_128x128(x, q=None, sf=None):
         sf = torch.empty(shape_sf, dtype=torch.float32, device=x.device)
     args = (_ptr(x, torch.float32, "x"), groups, rows, K, _ptr(q, _FP8, "q", tuple(x.shape)),
             _ptr(sf, torch.float32, "sf", shape_sf), _stream(x))
-    _check(lib().dg_quantize_e4m3_128x128(*args), "dg_quantize_e4m3_128x128")
+    name = _name("dg_quantize_e4m3_128x128", ue8m0)
+    _check(getattr(lib(), name)(*args), name)
     return q, sf
 
 

@@ -67,45 +67,80 @@ int check_k(int K) { return (K < 128 || K % 128 != 0) ? DG_ERR_SHAPE : DG_OK; }
 
 extern "C" {
 
-int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
-                   const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+static int gemm_nt_impl(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                        const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream, bool ue8m0) {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_NULL;
     if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (ld_sfa < M || ld_sfa % 4 != 0) return DG_ERR_ALIGN;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
         (c && !aligned16(c)))
         return DG_ERR_ALIGN;
-    dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0};
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, ue8m0};
     return run_gemm(p, stream);
 }
 
-int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
-                                        const uint16_t *c, uint16_t *d, const int32_t *m_indices, int M_total,
-                                        int N, int K, int G, void *stream) {
+static int contiguous_impl(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                           const uint16_t *c, uint16_t *d, const int32_t *m_indices, int M_total, int N, int K,
+                           int G, void *stream, bool ue8m0) {
     if (!a || !sfa || !b || !sfb || !d || !m_indices) return DG_ERR_NULL;
     if (M_total < 1 || M_total % 128 != 0 || N < 1 || G < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
         !aligned16(m_indices) || (c && !aligned16(c)))
         return DG_ERR_ALIGN;
-    dg::GemmProblem p{a, sfa, b, sfb, c, d, m_indices, M_total, N, K, M_total, G, dg::Mode::Contig, 0};
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, m_indices, M_total, N, K, M_total, G, dg::Mode::Contig, 0, ue8m0};
     return run_gemm(p, stream);
 }
 
-int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
-                                    const uint16_t *c, uint16_t *d, const int32_t *masked_m, int G, int M_cap,
-                                    int N, int K, int expected_m, void *stream) {
+static int masked_impl(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb, const uint16_t *c,
+                       uint16_t *d, const int32_t *masked_m, int G, int M_cap, int N, int K, int expected_m,
+                       void *stream, bool ue8m0) {
     if (!a || !sfa || !b || !sfb || !d || !masked_m) return DG_ERR_NULL;
     if (G < 1 || M_cap < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
         (c && !aligned16(c)))
         return DG_ERR_ALIGN;
     const int ld = (M_cap + 3) / 4 * 4;
-    dg::GemmProblem p{a, sfa, b, sfb, c, d, masked_m, M_cap, N, K, ld, G, dg::Mode::Masked, expected_m};
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, masked_m, M_cap, N, K, ld, G, dg::Mode::Masked, expected_m, ue8m0};
     return run_gemm(p, stream);
 }
 
-int dg_quantize_e4m3_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, int ld_sf,
-                           void *stream) {
+int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false);
+}
+
+int dg_fp8_gemm_nt_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                                        const uint16_t *c, uint16_t *d, const int32_t *m_indices, int M_total,
+                                        int N, int K, int G, void *stream) {
+    return contiguous_impl(a, sfa, b, sfb, c, d, m_indices, M_total, N, K, G, stream, false);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t *a, const float *sfa, const uint8_t *b,
+                                              const float *sfb, const uint16_t *c, uint16_t *d,
+                                              const int32_t *m_indices, int M_total, int N, int K, int G,
+                                              void *stream) {
+    return contiguous_impl(a, sfa, b, sfb, c, d, m_indices, M_total, N, K, G, stream, true);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                                    const uint16_t *c, uint16_t *d, const int32_t *masked_m, int G, int M_cap,
+                                    int N, int K, int expected_m, void *stream) {
+    return masked_impl(a, sfa, b, sfb, c, d, masked_m, G, M_cap, N, K, expected_m, stream, false);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                                          const uint16_t *c, uint16_t *d, const int32_t *masked_m, int G,
+                                          int M_cap, int N, int K, int expected_m, void *stream) {
+    return masked_impl(a, sfa, b, sfb, c, d, masked_m, G, M_cap, N, K, expected_m, stream, true);
+}
+
+static int quantize_1x128_impl(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, int ld_sf,
+                               void *stream, bool ue8m0) {
     if (!x || !q || !sf) return DG_ERR_NULL;
     if (groups < 1 || rows < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (ld_sf < rows || ld_sf % 4 != 0) return DG_ERR_ALIGN;
@@ -113,22 +148,43 @@ int dg_quantize_e4m3_1x128(const float *x, int groups, int rows, int K, uint8_t 
     int dev = 0, cus = 0;
     const int st = current_device(dev, cus);
     if (st != DG_OK) return st;
-    return dg::launch_quant_1x128(x, groups, rows, K, q, sf, ld_sf, static_cast<hipStream_t>(stream)) ==
+    return dg::launch_quant_1x128(x, groups, rows, K, q, sf, ld_sf, static_cast<hipStream_t>(stream), ue8m0) ==
                    hipSuccess
                ? DG_OK
                : DG_ERR_HIP;
 }
 
-int dg_quantize_e4m3_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, void *stream) {
+static int quantize_128x128_impl(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, void *stream,
+                                 bool ue8m0) {
     if (!x || !q || !sf) return DG_ERR_NULL;
     if (groups < 1 || rows < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return DG_ERR_ALIGN;
     int dev = 0, cus = 0;
     const int st = current_device(dev, cus);
     if (st != DG_OK) return st;
-    return dg::launch_quant_128x128(x, groups, rows, K, q, sf, static_cast<hipStream_t>(stream)) == hipSuccess
+    return dg::launch_quant_128x128(x, groups, rows, K, q, sf, static_cast<hipStream_t>(stream), ue8m0) ==
+                   hipSuccess
                ? DG_OK
                : DG_ERR_HIP;
+}
+
+int dg_quantize_e4m3_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, int ld_sf,
+                           void *stream) {
+    return quantize_1x128_impl(x, groups, rows, K, q, sf, ld_sf, stream, false);
+}
+
+int dg_quantize_e4m3_1x128_ue8m0(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, int ld_sf,
+                                 void *stream) {
+    return quantize_1x128_impl(x, groups, rows, K, q, sf, ld_sf, stream, true);
+}
+
+int dg_quantize_e4m3_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf, void *stream) {
+    return quantize_128x128_impl(x, groups, rows, K, q, sf, stream, false);
+}
+
+int dg_quantize_e4m3_128x128_ue8m0(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
+                                   void *stream) {
+    return quantize_128x128_impl(x, groups, rows, K, q, sf, stream, true);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

@@ -37,6 +37,15 @@ __device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i &a, const v8i &b, c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same product with E8M0 block scales applied by the matrix core:
+// c + sum_k (a_k * 2^(sa-127)) * (b_k * 2^(sb-127)), where sa (sb) is the
+// low byte of the first (second) operand's scale register, supplied per lane
+// for the 32 K elements that lane holds.
+__device__ __forceinline__ v4f mfma_16x16x128_e4m3_scaled(const v8i &a, const v8i &b, const v4f &c, int sa,
+                                                          int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // Promotion of a block partial: acc + p * s, as whole-vector values
 // (element stores into an accumulator array would keep it in memory); one
 // scale for all four elements, or one each.

@@ -9,10 +9,11 @@
 
 namespace dg {
 
+// ue8m0: the block scale rounded up to a power of two
 hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
-                              int ld_sf, hipStream_t stream);
+                              int ld_sf, hipStream_t stream, bool ue8m0);
 hipError_t launch_quant_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
-                                hipStream_t stream);
+                                hipStream_t stream, bool ue8m0);
 
 enum class Mode : int { Dense = 0, Contig = 1, Masked = 2 };
 
@@ -30,6 +31,10 @@ struct GemmProblem {
     int rows_a, N, K, ld_sfa, G;
     Mode mode;
     int expected_m;   // masked only: host hint, <= 0 unknown
+    // every scale is a power of two (UE8M0 quantisation): the pipelined
+    // family then applies them in the MFMA itself; other families promote
+    // in fp32 as usual, which is exact for such scales
+    bool ue8m0 = false;
 };
 
 // Skinny-M family: dense with M <= 128, and the masked layout; needs K >= 256

@@ -111,7 +111,7 @@ __device__ __forceinline__ int contig_unit_block(const int32_t *idx, int nblocks
     return -1;
 }
 
-template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT>
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 pipe_kernel(PipeParams p) {
     constexpr int NW = WGM * WGN;
@@ -404,8 +404,43 @@ pipe_kernel(PipeParams p) {
         }
     };
 
+    // Power-of-two scales: the MFMA applies them itself (E8M0 exponents, the
+    // biased fp32 exponent field of each scale: one for the wave's B block,
+    // one per lane for its A row) and accumulates straight into acc, so no
+    // fresh partial per K block and no promotion on the VALU.
+    auto compute_block_ue = [&](const uint8_t *stg_step, auto kkc) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kkc)::value;
+        const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
+        const int eb = (int)(__float_as_uint(sb) >> 23);
+        const uint8_t *stg = stg_step + kk * BLK_A;
+        const uint8_t *stg_b = stg_step + kk * BLK_B;
+        const uint8_t *stg_s = stg_step + kk * 1024;
+        v8i bf[SN];
+        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b0[0] + j * 16 * kKBlock);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b0[1] + j * 16 * kKBlock);
+            bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        });
+        static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a0[0] + i * 16 * kKBlock);
+            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
+            const v8i af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const float sa = *reinterpret_cast<const float *>(stg_s + off_sa0 + i * 64);
+            const int ea = (int)(__float_as_uint(sa) >> 23);
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                acc[i][j] = mfma_16x16x128_e4m3_scaled(bf[j], af, acc[i][j], eb, ea);
+            });
+        });
+    };
+
     auto compute = [&](const uint8_t *stg) __attribute__((always_inline)) {
-        static_for<KS>([&](auto kkc) __attribute__((always_inline)) { compute_block(stg, kkc); });
+        static_for<KS>([&](auto kkc) __attribute__((always_inline)) {
+            if constexpr (UE) compute_block_ue(stg, kkc);
+            else compute_block(stg, kkc);
+        });
     };
 
     // ---- K loop over NST stages: local step j (global step st0 + j) lives in
@@ -551,7 +586,7 @@ bool pipe_eligible(const GemmProblem &p) {
 // split over about units/tiles workgroups (some tiles one more than others,
 // so that exactly `units` workgroups run), each split keeping at least one
 // step; otherwise, or when no workspace is available, there is no split.
-template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT>
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false>
 hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, std::string &config) {
     PipeParams k;
     k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.d = p.d; k.idx = p.idx;
@@ -598,24 +633,24 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
     char buf[220];
     snprintf(buf, sizeof buf,
              "family=pipe mode=%d tile=%dx%dx128 waves=%dx%d stages=%d kblocks_per_stage=%d deep=%d splits=%d%s "
-             "grid=%lld",
+             "grid=%lld%s",
              (int)MODE, BM, BN, WGM, WGN, NST, KS, (int)DEEP, split ? k.splits_lo : 1,
-             split && k.split_hi > 0 ? "+" : "", (long long)grid);
+             split && k.split_hi > 0 ? "+" : "", (long long)grid, UE ? " scales=ue8m0" : "");
     config = buf;
     if constexpr (SPLIT) {
         if (split) {
-            hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true, UE>), dim3((unsigned)grid),
                                dim3(64 * WGM * WGN), 0, stream, k);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, false, UE>), dim3((unsigned)grid),
                            dim3(64 * WGM * WGN), 0, stream, k);
     return hipGetLastError();
 }
 
-hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
-    if (!pipe_eligible(p)) return hipErrorInvalidValue;
+template <bool UE>
+static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     const int cus = num_cus > 0 ? num_cus : 256;
     const int nkb = p.K / kKBlock;
     switch (p.mode) {
@@ -625,17 +660,17 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
         // (N, K) in {(2112, 7168), (7168, 16384)})
         if (p.rows_a <= 64) {
             if (nkb % 2 == 0) {
-                if (p.N < 4096) return launch_pipe_t<64, 64, 2, 4, 2, 2, false, Mode::Dense, true>(p, cus, stream, config);
-                return launch_pipe_t<64, 128, 2, 4, 3, 2, false, Mode::Dense, true>(p, cus, stream, config);
+                if (p.N < 4096) return launch_pipe_t<64, 64, 2, 4, 2, 2, false, Mode::Dense, true, UE>(p, cus, stream, config);
+                return launch_pipe_t<64, 128, 2, 4, 3, 2, false, Mode::Dense, true, UE>(p, cus, stream, config);
             }
-            return launch_pipe_t<64, 128, 2, 4, 4, 1, false, Mode::Dense, true>(p, cus, stream, config);
+            return launch_pipe_t<64, 128, 2, 4, 4, 1, false, Mode::Dense, true, UE>(p, cus, stream, config);
         }
         if (p.rows_a <= 128) {
             if (nkb % 2 == 0) {
-                if (p.N < 4096) return launch_pipe_t<128, 64, 4, 2, 3, 2, true, Mode::Dense, true>(p, cus, stream, config);
-                return launch_pipe_t<128, 128, 2, 4, 2, 2, true, Mode::Dense, true>(p, cus, stream, config);
+                if (p.N < 4096) return launch_pipe_t<128, 64, 4, 2, 3, 2, true, Mode::Dense, true, UE>(p, cus, stream, config);
+                return launch_pipe_t<128, 128, 2, 4, 2, 2, true, Mode::Dense, true, UE>(p, cus, stream, config);
             }
-            return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true>(p, cus, stream, config);
+            return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true, UE>(p, cus, stream, config);
         }
         // prefill shapes.  256x256 tiles (8 waves of 128x64, two stages) read
         // the fewest bytes from LDS and from L2 per MFMA.  With short K (few
@@ -646,20 +681,25 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
         // (7168, 2048), (24576, 1536)}).
         const int64_t t256 = (int64_t)((p.rows_a + 255) / 256) * ((p.N + 255) / 256);
         if (p.rows_a >= 256 && (nkb > 16 || t256 % cus == 0))
-            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
-        return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false>(p, 0, stream, config);
+            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, UE>(p, 0, stream, config);
+        return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, UE>(p, 0, stream, config);
     }
     case Mode::Contig:
         // 256-row units that never mix experts (the segments are 128-row
         // aligned); measured on MI355X for 8 experts, N = 4096, K = 7168:
         // 540 us against 575 us with 128x256 tiles
         if (p.rows_a >= 256)
-            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Contig, false>(p, 0, stream, config);
-        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false>(p, 0, stream, config);
+            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Contig, false, UE>(p, 0, stream, config);
+        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false, UE>(p, 0, stream, config);
     case Mode::Masked:
-        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false>(p, 0, stream, config);
+        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false, UE>(p, 0, stream, config);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
+    if (!pipe_eligible(p)) return hipErrorInvalidValue;
+    return p.ue8m0 ? launch_pipe_ue<true>(p, num_cus, stream, config) : launch_pipe_ue<false>(p, num_cus, stream, config);
 }
 
 }  // namespace dg

@@ -9,6 +9,11 @@
 // constraints") leaves this cast to the caller; these kernels write the
 // scale layouts that the GEMM entry points read.
 //
+// Power-of-two (UE8M0) variant: sf is the same quotient rounded up to the
+// next power of two (the packed-UE8M0 scaling of the README summary's SM100
+// kernels), so that the GEMM can hand the scales to the matrix cores'
+// exponent-scaled FP8 MFMA; dividing by it is exact.
+//
 // Both kernels are HBM-bound: 4 bytes read and 1 byte written per element.
 #include "dg_device.h"
 #include "dg_internal.h"
@@ -40,12 +45,19 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
     return sign | code;
 }
 
+template <bool UE8M0>
 __device__ __forceinline__ float block_scale(float amax) {
-    return fmaxf(amax, 1e-4f) / 448.0f;                   // IEEE division (no fast-math)
+    const float s = fmaxf(amax, 1e-4f) / 448.0f;          // IEEE division (no fast-math)
+    if constexpr (!UE8M0) return s;
+    // s is a normal fp32 (>= 1e-4/448): clear the mantissa and, if it was not
+    // zero, step the exponent up by one
+    const uint32_t u = __float_as_uint(s);
+    return __uint_as_float((u & 0x7fffffu) ? (u & 0x7f800000u) + 0x00800000u : u);
 }
 
 // 1x128: a half-wave (32 lanes x float4) per 128-element block; consecutive
 // half-waves take consecutive blocks of a row, so loads and stores coalesce.
+template <bool UE8M0>
 __global__ void __launch_bounds__(256)
 quant_1x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ sf,
                    int rows, int nkb, int ld_sf, int64_t nblocks) {
@@ -56,7 +68,7 @@ quant_1x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *
     float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
-    const float s = block_scale(amax);
+    const float s = block_scale<UE8M0>(amax);
     const uint32_t packed = e4m3_encode(v.x / s) | (e4m3_encode(v.y / s) << 8) |
                             (e4m3_encode(v.z / s) << 16) | (e4m3_encode(v.w / s) << 24);
     reinterpret_cast<uint32_t *>(q + blk * kKBlock)[l] = packed;
@@ -72,6 +84,7 @@ quant_1x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *
 // 128x128: one 256-thread workgroup per block.  Thread t covers rows
 // t/32 + 8i (i < 16) at column chunk t%32, keeping its 64 values in registers
 // between the amax reduction and the encode.
+template <bool UE8M0>
 __global__ void __launch_bounds__(256)
 quant_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ sf,
                      int rows, int K, int nrb, int nkb) {
@@ -98,7 +111,7 @@ quant_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float
     if ((t & 63) == 0) wmax[t >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float s = block_scale(amax);
+    const float s = block_scale<UE8M0>(amax);
     uint8_t *qg = q + g * rows * (int64_t)K;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -113,24 +126,32 @@ quant_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float
 }
 
 hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
-                              int ld_sf, hipStream_t stream) {
+                              int ld_sf, hipStream_t stream, bool ue8m0) {
     const int nkb = K / kKBlock;
     const int64_t nblocks = (int64_t)groups * rows * nkb;
     const int64_t grid = (nblocks + 7) / 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_1x128_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       x, q, sf, rows, nkb, ld_sf, nblocks);
+    if (ue8m0)
+        hipLaunchKernelGGL(quant_1x128_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           x, q, sf, rows, nkb, ld_sf, nblocks);
+    else
+        hipLaunchKernelGGL(quant_1x128_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           x, q, sf, rows, nkb, ld_sf, nblocks);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool ue8m0) {
     const int nkb = K / kKBlock;
     const int nrb = (rows + 127) / 128;
     const int64_t grid = (int64_t)groups * nrb * nkb;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_128x128_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       x, q, sf, rows, K, nrb, nkb);
+    if (ue8m0)
+        hipLaunchKernelGGL(quant_128x128_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           x, q, sf, rows, K, nrb, nkb);
+    else
+        hipLaunchKernelGGL(quant_128x128_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           x, q, sf, rows, K, nrb, nkb);
     return hipGetLastError();
 }
 

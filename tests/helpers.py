@@ -77,32 +77,32 @@ class Guarded:
 
 # ------------------------------------------------------------ problems
 
-def dense_problem(M, N, K, seed, with_c):
+def dense_problem(M, N, K, seed, with_c, ue8m0=False):
     xa = synth.normal_f32(seed, synth.STREAM_A, (M, K))
     xb = synth.normal_f32(seed, synth.STREAM_B, (N, K))
-    a, sfa = oracle.quantize_1x128(xa)
-    b, sfb = oracle.quantize_128x128(xb)
+    a, sfa = oracle.quantize_1x128(xa, ue8m0=ue8m0)
+    b, sfb = oracle.quantize_128x128(xb, ue8m0=ue8m0)
     c = synth.normal_bf16_bits(seed, synth.STREAM_C, (M, N)) if with_c else None
     return dict(a=a, sfa=sfa, b=b, sfb=sfb, c=c, M=M, N=N, K=K)
 
 
-def contiguous_problem(counts, N, K, seed, with_c=False):
+def contiguous_problem(counts, N, K, seed, with_c=False, ue8m0=False):
     m_idx = synth.contiguous_m_indices(counts)
     M_total = m_idx.size
     G = len(counts)
     xa = synth.normal_f32(seed, synth.STREAM_A, (M_total, K))
     xb = synth.normal_f32(seed, synth.STREAM_B, (G, N, K))
-    a, sfa = oracle.quantize_1x128(xa)
-    b, sfb = oracle.quantize_128x128(xb)
+    a, sfa = oracle.quantize_1x128(xa, ue8m0=ue8m0)
+    b, sfb = oracle.quantize_128x128(xb, ue8m0=ue8m0)
     c = synth.normal_bf16_bits(seed, synth.STREAM_C, (M_total, N)) if with_c else None
     return dict(a=a, sfa=sfa, b=b, sfb=sfb, c=c, m_indices=m_idx, M_total=M_total, N=N, K=K, G=G)
 
 
-def masked_problem(G, M_cap, N, K, masked_m, seed, with_c=False):
+def masked_problem(G, M_cap, N, K, masked_m, seed, with_c=False, ue8m0=False):
     xa = synth.normal_f32(seed, synth.STREAM_A, (G, M_cap, K))
     xb = synth.normal_f32(seed, synth.STREAM_B, (G, N, K))
-    a, sfa = oracle.quantize_1x128(xa)
-    b, sfb = oracle.quantize_128x128(xb)
+    a, sfa = oracle.quantize_1x128(xa, ue8m0=ue8m0)
+    b, sfb = oracle.quantize_128x128(xb, ue8m0=ue8m0)
     c = synth.normal_bf16_bits(seed, synth.STREAM_C, (G, M_cap, N)) if with_c else None
     return dict(a=a, sfa=sfa, b=b, sfb=sfb, c=c, masked_m=np.asarray(masked_m, dtype=np.int32),
                 G=G, M_cap=M_cap, N=N, K=K)
