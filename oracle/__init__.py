@@ -49,6 +49,8 @@ def _load():
         "orc_m_grouped_contiguous_at": (None, [P, P, P, P, P, P, I, I, I, I, P, P, L, P]),
         "orc_m_grouped_masked": (None, [P, P, P, P, P, P, P, I, I, I, I]),
         "orc_m_grouped_masked_at": (None, [P, P, P, P, P, P, I, I, I, I, P, P, P, L, P]),
+        "orc_mqa_logits": (None, [P, P, P, P, P, P, I, I, I, I, I, P]),
+        "orc_mqa_logits_rows": (None, [P, P, P, P, P, P, I, I, I, I, P, I, P]),
         "orc_num_threads": (I, []),
     }
     for name, (res, args) in sig.items():
@@ -219,6 +221,41 @@ def m_grouped_masked_at(a, sfa, b, sfb, c, masked_m, gs, ms, ns):
                                     _p(masked_m, _np.int32), G, M_cap, N, K,
                                     gs.ctypes.data, ms.ctypes.data, ns.ctypes.data, ms.size,
                                     out.ctypes.data)
+    return out
+
+
+def _mqa_args(q, kv, kv_scale, weights, k_start, k_end):
+    q = _np.ascontiguousarray(q, dtype=_np.uint8)
+    kv = _np.ascontiguousarray(kv, dtype=_np.uint8)
+    kv_scale = _np.ascontiguousarray(kv_scale, dtype=_np.float32)
+    weights = _np.ascontiguousarray(weights, dtype=_np.float32)
+    k_start = _np.ascontiguousarray(k_start, dtype=_np.int32)
+    k_end = _np.ascontiguousarray(k_end, dtype=_np.int32)
+    S, H, D = q.shape
+    Skv = kv.shape[0]
+    assert kv.shape == (Skv, D) and kv_scale.shape == (Skv,) and weights.shape == (S, H)
+    assert k_start.shape == (S,) and k_end.shape == (S,)
+    return q, kv, kv_scale, weights, k_start, k_end, S, H, D, Skv
+
+
+def mqa_logits(q, kv, kv_scale, weights, k_start, k_end, clean_logits):
+    """FP8 MQA logits [S, Skv] in fp64; positions left untouched are NaN."""
+    q, kv, kv_scale, weights, k_start, k_end, S, H, D, Skv = _mqa_args(q, kv, kv_scale, weights, k_start, k_end)
+    out = _np.full((S, Skv), _np.nan, dtype=_np.float64)
+    _load().orc_mqa_logits(q.ctypes.data, kv.ctypes.data, kv_scale.ctypes.data, weights.ctypes.data,
+                           k_start.ctypes.data, k_end.ctypes.data, int(bool(clean_logits)), S, H, D, Skv,
+                           out.ctypes.data)
+    return out
+
+
+def mqa_logits_rows(q, kv, kv_scale, weights, k_start, k_end, clean_logits, rows):
+    """The listed query rows of mqa_logits: [len(rows), Skv] fp64 (untouched: NaN)."""
+    q, kv, kv_scale, weights, k_start, k_end, S, H, D, Skv = _mqa_args(q, kv, kv_scale, weights, k_start, k_end)
+    rows = _np.ascontiguousarray(rows, dtype=_np.int32)
+    out = _np.full((rows.size, Skv), _np.nan, dtype=_np.float64)
+    _load().orc_mqa_logits_rows(q.ctypes.data, kv.ctypes.data, kv_scale.ctypes.data, weights.ctypes.data,
+                                k_start.ctypes.data, k_end.ctypes.data, int(bool(clean_logits)), H, D, Skv,
+                                rows.ctypes.data, rows.size, out.ctypes.data)
     return out
 
 

@@ -380,6 +380,76 @@ void orc_m_grouped_masked_at(const uint8_t *a, const float *sfa,
                      : masked_elem(a, sfa, b, sfb, c, G, M_cap, N, K, gs[i], ms[i], ns[i]);
 }
 
+/* ---------------------------------------------------------------------- */
+/* FP8 MQA logits (the DeepSeek v3.2 indexer's scoring kernel; GeekNews   */
+/* summary of the DeepGEMM README, ja.news.hada.io topic 19459, section on */
+/* the MQA kernels for the v3.2 Indexer, non-paged form).  For query token */
+/* i and every key token j in                                              */
+/* [k_start[i], k_end[i]) (clamped to [0, Skv]):                           */
+/*   logits[i][j] = sum_h weights[i][h] * ReLU(kv_scale[j] * (q[i,h,:] . kv[j,:]))  */
+/* The dot product of E4M3 values is exact in fp64 (products are multiples */
+/* of 2^-18, as in the GEMM); scale, ReLU, weight and the head sum are     */
+/* fp64, heads in order.  Other positions of row i are set to -inf when    */
+/* clean_logits is non-zero and left untouched otherwise.                  */
+/* ---------------------------------------------------------------------- */
+
+static void mqa_range(const int32_t *k_start, const int32_t *k_end, int i, int Skv, int *j0, int *j1)
+{
+    int a = k_start[i], b = k_end[i];
+    a = a < 0 ? 0 : (a > Skv ? Skv : a);
+    b = b < 0 ? 0 : (b > Skv ? Skv : b);
+    *j0 = a;
+    *j1 = b > a ? b : a;
+}
+
+static void mqa_row(const uint8_t *q, const uint8_t *kv, const float *kv_scale, const float *weights,
+                    const int32_t *k_start, const int32_t *k_end, int clean_logits,
+                    int H, int D, int Skv, int i, double *row)
+{
+    int j0, j1;
+    mqa_range(k_start, k_end, i, Skv, &j0, &j1);
+    for (int j = 0; j < Skv; ++j) {
+        if (j < j0 || j >= j1) {
+            if (clean_logits)
+                row[j] = -INFINITY;
+            continue;
+        }
+        double logit = 0.0;
+        for (int h = 0; h < H; ++h) {
+            const uint8_t *qv = q + ((size_t)i * H + h) * (size_t)D;
+            const uint8_t *kr = kv + (size_t)j * D;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += T[qv[d]] * T[kr[d]];
+            const double s = (double)kv_scale[j] * dot;
+            logit += (double)weights[(size_t)i * H + h] * (s > 0.0 ? s : 0.0);
+        }
+        row[j] = logit;
+    }
+}
+
+void orc_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *kv_scale, const float *weights,
+                    const int32_t *k_start, const int32_t *k_end, int clean_logits,
+                    int S, int H, int D, int Skv, double *out)
+{
+    table_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < S; ++i)
+        mqa_row(q, kv, kv_scale, weights, k_start, k_end, clean_logits, H, D, Skv, i,
+                out + (size_t)i * Skv);
+}
+
+void orc_mqa_logits_rows(const uint8_t *q, const uint8_t *kv, const float *kv_scale, const float *weights,
+                         const int32_t *k_start, const int32_t *k_end, int clean_logits,
+                         int H, int D, int Skv, const int32_t *rows, int nrows, double *out)
+{
+    table_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r)
+        mqa_row(q, kv, kv_scale, weights, k_start, k_end, clean_logits, H, D, Skv, rows[r],
+                out + (size_t)r * Skv);
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -1,6 +1,6 @@
 /*
- * oracle.h -- plain CPU reference for the FP8 block-scaled NT GEMM and its
- * M-grouped variants.
+ * oracle.h -- plain CPU reference for the FP8 block-scaled NT GEMM, its
+ * M-grouped variants, the E4M3 quantisers and the FP8 MQA logits.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
@@ -14,6 +14,8 @@
  *  - same page, section "Dense and Grouped GEMM": M-grouped contiguous layout
  *    (expert segments aligned to the M block) and masked layout (only the
  *    valid rows of each group are computed).
+ *  - same page, section on the MQA kernels for the DeepSeek v3.2 Indexer:
+ *    the non-paged fp8_mqa_logits inputs, shapes and per-token formula.
  *  - "DeepSeek open-sources DeepGEMM" news (picoinsstore.com), paragraph on
  *    the two-level accumulation: the low-precision tensor-core partial is
  *    promoted into a higher-precision accumulator.
@@ -30,7 +32,8 @@
  * its formula (exhaustive codec checks against torch's float8_e4m3fn,
  * closed-form scale cases, numpy matmul of the de-scaled operands, integer
  * evaluation of block sums, identity/one-hot products, grouped == per-group
- * dense).  None is "parity unpinned".
+ * dense; for the MQA logits: brute force over torch's E4M3 decode, one-hot
+ * closed forms, ReLU, linearity and range-masking properties).  None is "parity unpinned".
  */
 #ifndef DG_ORACLE_H
 #define DG_ORACLE_H
@@ -132,6 +135,21 @@ void orc_m_grouped_masked_at(const uint8_t *a, const float *sfa,
                              int G, int M_cap, int N, int K,
                              const int32_t *gs, const int32_t *ms,
                              const int32_t *ns, int64_t count, double *out);
+
+/* FP8 MQA logits, non-paged (GeekNews summary of the DeepGEMM README, section
+ * on the MQA kernels for the DeepSeek v3.2 Indexer):
+ *   q [S][H][D] E4M3, kv [Skv][D] E4M3, kv_scale [Skv] fp32, weights [S][H] fp32,
+ *   k_start, k_end [S] int32; out [S][Skv] fp64:
+ *   out[i][j] = sum_h weights[i][h] * ReLU(kv_scale[j] * (q[i,h,:] . kv[j,:]))
+ * for j in [k_start[i], k_end[i]) clamped to [0, Skv]; other positions -inf
+ * when clean_logits, else untouched.  The _rows form evaluates the listed
+ * query rows into out[nrows][Skv]. */
+void orc_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *kv_scale, const float *weights,
+                    const int32_t *k_start, const int32_t *k_end, int clean_logits,
+                    int S, int H, int D, int Skv, double *out);
+void orc_mqa_logits_rows(const uint8_t *q, const uint8_t *kv, const float *kv_scale, const float *weights,
+                         const int32_t *k_start, const int32_t *k_end, int clean_logits,
+                         int H, int D, int Skv, const int32_t *rows, int nrows, double *out);
 
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int orc_num_threads(void);

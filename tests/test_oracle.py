@@ -477,3 +477,142 @@ def test_masked_negative_count_is_zero_rows():
     sfb = np.ones((1, 1, 1), dtype=np.float32)
     d = oracle.m_grouped_masked(a, sfa, b, sfb, None, np.array([-3], dtype=np.int32))
     assert np.all(np.isnan(d))
+
+
+# ---------------------------------------------------------------- MQA logits
+# The non-paged FP8 MQA logits of the DeepSeek v3.2 indexer (GeekNews summary
+# of the DeepGEMM README, section on the MQA kernels for the v3.2 Indexer):
+# for query token i and key token j in [k_start[i], k_end[i]), the logit is
+# the weights[i]-weighted sum over heads of ReLU(kv_scale[j] * q[i,h].kv[j]).
+
+
+def _mqa_inputs(seed, S, H, D, Skv):
+    q = synth.random_codes(seed, 0, (S, H, D))
+    kv = synth.random_codes(seed, 1, (Skv, D))
+    kv_scale = (0.5 + synth.uniform(seed, 2, Skv)).astype(np.float32)
+    weights = synth.normal_f32(seed, 3, (S, H))
+    ks = synth.randint(seed, 4, S, -2, Skv // 2).astype(np.int32)
+    ke = (ks + synth.randint(seed, 5, S, -1, Skv + 3)).astype(np.int32)
+    return q, kv, kv_scale, weights, ks, ke
+
+
+@pytest.mark.parametrize("clean", [True, False])
+def test_mqa_logits_brute_force_over_torch_decode(clean):
+    """Tiny case evaluated with torch's E4M3 decode and integer dot products
+    (E4M3 values are multiples of 2^-9, so q.kv * 2^18 is an exact integer);
+    the scale, ReLU, weighting and head sum follow in fp64, heads in order."""
+    S, H, D, Skv = 6, 3, 256, 11
+    q, kv, kv_scale, weights, ks, ke = _mqa_inputs(50, S, H, D, Skv)
+    got = oracle.mqa_logits(q, kv, kv_scale, weights, ks, ke, clean)
+    qi = (torch_decode(q) * 512).astype(np.int64)
+    ki = (torch_decode(kv) * 512).astype(np.int64)
+    for i in range(S):
+        lo, hi = min(max(int(ks[i]), 0), Skv), min(max(int(ke[i]), 0), Skv)
+        for j in range(Skv):
+            if not (lo <= j < hi):
+                if clean:
+                    assert got[i, j] == -np.inf
+                else:
+                    assert np.isnan(got[i, j])
+                continue
+            want = 0.0
+            for h in range(H):
+                dot = float(int(np.dot(qi[i, h], ki[j]))) * 2.0 ** -18
+                want += float(weights[i, h]) * max(float(kv_scale[j]) * dot, 0.0)
+            assert got[i, j] == want, (i, j, got[i, j], want)
+
+
+def test_mqa_logits_one_hot_closed_form():
+    """q[i,h] has a single non-zero x_{i,h} at position p(i,h), kv[j] a single
+    non-zero y_j at position r(j): the dot is x*y when the positions meet and
+    0 otherwise, so each logit is a short sum fixed in advance."""
+    S, H, D, Skv = 4, 2, 128, 5
+    q = np.zeros((S, H, D), np.uint8)
+    kv = np.zeros((Skv, D), np.uint8)
+    pos_q = [[3, 7], [7, 3], [100, 3], [5, 5]]
+    val_q = [[0x40, 0xC0], [0x38, 0x48], [0x30, 0x38], [0x38, 0xB8]]  # 2,-2 | 1,4 | 0.5,1 | 1,-1
+    pos_kv = [3, 7, 5, 100, 3]
+    val_kv = [0x38, 0x40, 0x44, 0xB8, 0xC0]                             # 1, 2, 3, -1, -2
+    for i in range(S):
+        for h in range(H):
+            q[i, h, pos_q[i][h]] = val_q[i][h]
+    for j in range(Skv):
+        kv[j, pos_kv[j]] = val_kv[j]
+    kv_scale = np.array([1.0, 0.5, 2.0, 4.0, 0.25], np.float32)
+    weights = np.array([[1.0, 1.0], [0.5, 2.0], [1.0, -1.0], [3.0, 3.0]], np.float32)
+    ks = np.zeros(S, np.int32)
+    ke = np.full(S, Skv, np.int32)
+    got = oracle.mqa_logits(q, kv, kv_scale, weights, ks, ke, True)
+    want = np.array([
+        # i=0: h0 (2 at 3), h1 (-2 at 7)
+        [2 * 1 * 1.0, 0.0, 0.0, 0.0, 0.0],         # j=1: h1 gives -2*2*0.5<0; j=4: 2*-2*.25<0
+        # i=1: h0 (1 at 7) w .5, h1 (4 at 3) w 2
+        [2 * 4 * 1 * 1.0, 0.5 * 1 * 2 * 0.5, 0.0, 0.0, 0.0],   # j=4: 4*-2 <0
+        # i=2: h0 (0.5 at 100) w 1, h1 (1 at 3) w -1
+        [-1 * 1 * 1.0, 0.0, 0.0, 0.0, 0.0],        # j=3: 0.5*-1*4 <0 -> 0
+        # i=3: h0 (1 at 5), h1 (-1 at 5), w 3
+        [0.0, 0.0, 3 * 1 * 3 * 2.0, 0.0, 0.0],     # h1: -3*2 < 0 -> 0
+    ])
+    assert np.array_equal(got, want), got
+
+
+def test_mqa_logits_relu_cuts_negative_heads_only():
+    """kv = -q[i,0] makes head 0's product negative (dropped) and leaves a
+    head whose q equals kv with its full square norm."""
+    D = 128
+    x = synth.random_codes(51, 0, (D,))
+    neg = x ^ np.uint8(0x80)
+    q = np.stack([x, neg])[None]                 # [1, 2, D]: head 0 = x, head 1 = -x
+    kv = neg[None]                               # kv = -x
+    norm2 = float(np.sum(torch_decode(x) ** 2))
+    got = oracle.mqa_logits(q, kv, np.ones(1, np.float32), np.array([[5.0, 0.25]], np.float32),
+                            np.zeros(1, np.int32), np.ones(1, np.int32), True)
+    assert got[0, 0] == 0.25 * norm2
+
+
+def test_mqa_logits_linear_in_weights_and_homogeneous_in_scale():
+    S, H, D, Skv = 5, 4, 128, 7
+    q, kv, kv_scale, weights, ks, ke = _mqa_inputs(52, S, H, D, Skv)
+    ks[:] = 0
+    ke[:] = Skv
+    # weights that are small integers keep every sum exact
+    w1 = synth.randint(52, 9, S * H, -4, 5).reshape(S, H).astype(np.float32)
+    w2 = synth.randint(52, 10, S * H, -4, 5).reshape(S, H).astype(np.float32)
+    sc = np.ldexp(np.float32(1.0), synth.randint(52, 11, Skv, -3, 4)).astype(np.float32)
+    l1 = oracle.mqa_logits(q, kv, sc, w1, ks, ke, True)
+    l2 = oracle.mqa_logits(q, kv, sc, w2, ks, ke, True)
+    l12 = oracle.mqa_logits(q, kv, sc, w1 + w2, ks, ke, True)
+    assert np.array_equal(l12, l1 + l2)
+    l_half = oracle.mqa_logits(q, kv, (sc * 0.5).astype(np.float32), w1, ks, ke, True)
+    assert np.array_equal(l_half * 2, l1)
+    # a head with weight one and all others zero gives that head's ReLU(dot)
+    dots = np.einsum("shd,kd->shk", torch_decode(q), torch_decode(kv))
+    for h in range(H):
+        w = np.zeros((S, H), np.float32)
+        w[:, h] = 1.0
+        lh = oracle.mqa_logits(q, kv, np.ones(Skv, np.float32), w, ks, ke, True)
+        assert np.array_equal(lh, np.maximum(dots[:, h, :], 0.0))
+
+
+def test_mqa_logits_ranges_clamped_and_rows_form_agrees():
+    S, H, D, Skv = 7, 2, 128, 9
+    q, kv, kv_scale, weights, _, _ = _mqa_inputs(53, S, H, D, Skv)
+    ks = np.array([-5, 0, 3, 8, 9, 4, 20], np.int32)
+    ke = np.array([2, 9, 3, 100, 12, 1, 30], np.int32)
+    full = oracle.mqa_logits(q, kv, kv_scale, weights, np.zeros(S, np.int32), np.full(S, Skv, np.int32), True)
+    for clean in (True, False):
+        got = oracle.mqa_logits(q, kv, kv_scale, weights, ks, ke, clean)
+        for i in range(S):
+            lo, hi = min(max(ks[i], 0), Skv), min(max(ke[i], 0), Skv)
+            inside = np.zeros(Skv, bool)
+            inside[lo:max(lo, hi)] = True
+            assert np.array_equal(got[i, inside], full[i, inside])
+            if clean:
+                assert np.all(got[i, ~inside] == -np.inf)
+            else:
+                assert np.all(np.isnan(got[i, ~inside]))
+        # rows 2 (empty), 4 (start at Skv) and 5 (end before start) have no key
+        assert not np.any(np.isfinite(got[[2, 4, 5]]))
+        rows = np.array([6, 0, 3, 3], np.int32)
+        sub = oracle.mqa_logits_rows(q, kv, kv_scale, weights, ks, ke, clean, rows)
+        assert np.array_equal(sub, got[rows], equal_nan=True)
