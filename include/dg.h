@@ -176,6 +176,39 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t *a, const float *sfa,
                                           int G, int M_cap, int N, int K,
                                           int expected_m, void *stream);
 
+/*
+ * FP8 MQA logits, non-paged (the DeepSeek v3.2 indexer's scoring kernel;
+ * GeekNews summary of the DeepGEMM README, section on the MQA kernels for the
+ * v3.2 Indexer).  For every query token i and key token j in
+ * [k_start[i], k_end[i]) (both clamped to [0, S_kv]; empty when end <= start):
+ *   logits[i][j] = sum_h weights[i][h] * ReLU(kv_scale[j] * (q[i,h,:] . kv[j,:]))
+ *   q         [S][H][D]  E4M3
+ *   kv        [S_kv][D]  E4M3
+ *   kv_scale  [S_kv]     fp32, positive and finite (the kernel applies it
+ *                        after the ReLU and the head sum, which equals the
+ *                        formula only for positive scales; not checked)
+ *   weights   [S][H]     fp32
+ *   k_start, k_end [S]   int32
+ *   logits    [S][S_kv]  fp32 (row i at logits + i*S_kv).  Positions of row
+ *                        i outside its range are set to -inf when
+ *                        clean_logits != 0 and left untouched otherwise.
+ * Accuracy: the FP8 matrix instruction sums each group of 8 consecutive
+ * head-dim products in a window 13 bits below the group's leading bit
+ * (truncating) and the group sums in fp32; the weighted head sum is fp32.  A
+ * logit is within 2^-10 * kv_scale[j] * sum_h |weights[i][h]| *
+ * sum_d |q[i,h,d] kv[j,d]| of the exact value.
+ * Supported: D == 128, H in {16, 32, 48, 64}, S_kv * D < 2^31.
+ * Errors: DG_ERR_NULL (any pointer), DG_ERR_SHAPE (S, S_kv < 1; D, H
+ * unsupported; S_kv too large), DG_ERR_ALIGN (q, kv, weights not 16-B
+ * aligned; kv_scale, k_start, k_end, logits not 4-B aligned).  Rows are
+ * written with 16-byte stores when S_kv % 4 == 0 and logits is 16-B aligned,
+ * with 4-byte stores otherwise.
+ */
+int dg_fp8_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *kv_scale,
+                      const float *weights, const int32_t *k_start, const int32_t *k_end,
+                      int clean_logits, float *logits,
+                      int S, int H, int D, int S_kv, void *stream);
+
 /* Row alignment of expert segments in the contiguous layout (128).  The
  * setter accepts only 128 and returns DG_ERR_ARG otherwise. ("Utilities and
  * environment variables" section.) */

@@ -50,6 +50,9 @@ EXPORTS = {
                                                 ct.c_void_p, ct.c_int, ct.c_void_p]),
     "dg_quantize_e4m3_128x128_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
                                                   ct.c_void_p, ct.c_void_p]),
+    "dg_fp8_mqa_logits": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                     ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
+                                     ct.c_void_p]),
     "dg_get_mk_alignment_for_contiguous_layout": (ct.c_int, []),
     "dg_set_mk_alignment_for_contiguous_layout": (ct.c_int, [ct.c_int]),
     "dg_get_sf_aligned_size": (ct.c_int, [ct.c_int]),
@@ -200,6 +203,22 @@ def quantize_e4m3_128x128(x, q=None, sf=None, ue8m0=False):
     name = _name("dg_quantize_e4m3_128x128", ue8m0)
     _check(getattr(lib(), name)(*args), name)
     return q, sf
+
+
+def fp8_mqa_logits(q, kv, kv_scale, weights, k_start, k_end, clean_logits=True, logits=None):
+    """FP8 MQA logits (dg_fp8_mqa_logits).  q[S, H, D], kv[S_kv, D] E4M3, kv_scale[S_kv] fp32,
+    weights[S, H] fp32, k_start/k_end[S] int32 -> logits[S, S_kv] fp32 (allocated when None; when
+    clean_logits is false, positions outside a row's range keep what `logits` held)."""
+    S, H, D = tuple(q.shape)
+    S_kv = kv.shape[0]
+    if logits is None:
+        logits = torch.empty((S, S_kv), dtype=torch.float32, device=q.device)
+    args = (_ptr(q, _FP8, "q"), _ptr(kv, _FP8, "kv", (S_kv, D)), _ptr(kv_scale, torch.float32, "kv_scale", (S_kv,)),
+            _ptr(weights, torch.float32, "weights", (S, H)), _ptr(k_start, torch.int32, "k_start", (S,)),
+            _ptr(k_end, torch.int32, "k_end", (S,)), int(bool(clean_logits)),
+            _ptr(logits, torch.float32, "logits", (S, S_kv)), S, H, D, S_kv, _stream(q))
+    _check(lib().dg_fp8_mqa_logits(*args), "dg_fp8_mqa_logits")
+    return logits
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:

@@ -187,6 +187,27 @@ int dg_quantize_e4m3_128x128_ue8m0(const float *x, int groups, int rows, int K, 
     return quantize_128x128_impl(x, groups, rows, K, q, sf, stream, true);
 }
 
+int dg_fp8_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *kv_scale, const float *weights,
+                      const int32_t *k_start, const int32_t *k_end, int clean_logits, float *logits, int S, int H,
+                      int D, int S_kv, void *stream) {
+    if (!q || !kv || !kv_scale || !weights || !k_start || !k_end || !logits) return DG_ERR_NULL;
+    if (S < 1 || S_kv < 1 || D != 128 || H < 16 || H > 64 || H % 16 != 0) return DG_ERR_SHAPE;
+    if ((long long)S_kv * D >= (1LL << 31) || (long long)S * H * D >= (1LL << 62)) return DG_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(weights) || (reinterpret_cast<uintptr_t>(kv_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(k_start) & 3u) || (reinterpret_cast<uintptr_t>(k_end) & 3u) ||
+        (reinterpret_cast<uintptr_t>(logits) & 3u))
+        return DG_ERR_ALIGN;
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) return st;
+    std::string cfg;
+    const hipError_t err = dg::launch_mqa_logits(q, kv, kv_scale, weights, k_start, k_end, clean_logits, logits, S,
+                                                 H, S_kv, static_cast<hipStream_t>(stream), cfg);
+    t_last_config = cfg;
+    if (print_configs()) fprintf(stderr, "[dg] %s\n", cfg.c_str());
+    return err == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
 
 int dg_set_mk_alignment_for_contiguous_layout(int alignment) { return alignment == 128 ? DG_OK : DG_ERR_ARG; }

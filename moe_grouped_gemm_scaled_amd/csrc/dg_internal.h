@@ -15,6 +15,13 @@ hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8
 hipError_t launch_quant_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
                                 hipStream_t stream, bool ue8m0);
 
+// FP8 MQA logits (non-paged): q [S][H][128], kv [Skv][128] E4M3, kv_scale
+// [Skv] (positive), weights [S][H], ranges [S]; logits [S][Skv] fp32.  Needs
+// H in {16, 32, 48, 64} and Skv * 128 below 2^31.
+hipError_t launch_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *kv_scale, const float *weights,
+                             const int32_t *k_start, const int32_t *k_end, int clean_logits, float *logits, int S,
+                             int H, int Skv, hipStream_t stream, std::string &config);
+
 enum class Mode : int { Dense = 0, Contig = 1, Masked = 2 };
 
 // Arguments of one GEMM launch.  Per group, A has `rows_a` rows (dense: M,

@@ -145,3 +145,45 @@ def contiguous_counts(cfg=CONTIGUOUS) -> np.ndarray:
 
 def masked_counts(cfg=MASKED) -> np.ndarray:
     return randint(cfg["seed"], STREAM_COUNTS, cfg["G"], cfg["mm_lo"], cfg["mm_hi"]).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# MQA logits inputs (the v3.2 indexer's scoring: q [S, H, 128] and kv
+# [S_kv, 128] E4M3, kv_scale [S_kv], weights [S, H], key ranges [S])
+# --------------------------------------------------------------------------
+
+STREAM_Q, STREAM_KV, STREAM_KV_SCALE, STREAM_WEIGHTS = 10, 11, 12, 13
+
+# One prefill chunk of 4096 query tokens at the end of an 8192-token context,
+# causal: query i sees keys [0, S_kv - S + i + 1).  64 heads of dim 128 (the
+# indexer's head layout).
+MQA = dict(name="mqa_s4096_skv8192_h64", S=4096, S_kv=8192, H=64, D=128, seed=SEED_BASE + 5)
+
+
+def mqa_tensors(seed: int, S: int, H: int, S_kv: int, D: int = 128):
+    """q, kv (uniformly random E4M3 codes, no NaN), kv_scale (positive,
+    2^-9 (1 + u)), weights (N(0, 1) / sqrt(H))."""
+    q = random_codes(seed, STREAM_Q, (S, H, D))
+    kv = random_codes(seed, STREAM_KV, (S_kv, D))
+    kv_scale = ((1.0 + uniform(seed, STREAM_KV_SCALE, S_kv)) * 2.0 ** -9).astype(np.float32)
+    weights = (normal_f32(seed, STREAM_WEIGHTS, (S, H)) / np.float32(np.sqrt(H))).astype(np.float32)
+    return q, kv, kv_scale, weights
+
+
+def causal_ranges(S: int, S_kv: int):
+    """Queries are the last S of S_kv tokens: query i sees keys [0, S_kv - S + i + 1)."""
+    ks = np.zeros(S, dtype=np.int32)
+    ke = (S_kv - S + 1 + np.arange(S)).astype(np.int32)
+    return ks, ke
+
+
+def packed_ranges(lengths):
+    """Sequences packed back to back (S = S_kv = sum of lengths), causal within
+    each: query i of a sequence starting at b sees keys [b, i + 1)."""
+    ks, ke, b = [], [], 0
+    for L in lengths:
+        L = int(L)
+        ks.append(np.full(L, b, dtype=np.int32))
+        ke.append((b + 1 + np.arange(L)).astype(np.int32))
+        b += L
+    return np.concatenate(ks), np.concatenate(ke)

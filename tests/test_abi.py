@@ -121,3 +121,28 @@ def test_binding_rejects_wrong_tensors_on_host():
         binding._ptr(a, torch.uint8, "a")     # not a device tensor
     with pytest.raises(TypeError):
         binding._ptr(a, torch.float32, "a")
+
+
+def test_mqa_logits_argument_errors(lib):
+    f = lib.dg_fp8_mqa_logits
+    # q, kv, kv_scale, weights, k_start, k_end, clean, logits, S, H, D, S_kv, stream
+    ok = (P, P, P, P, P, P, 1, P, 64, 64, 128, 256, S)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["q", "kv", "sc", "w", "ks", "ke", "clean", "out", "S", "H", "D", "S_kv", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    for name in ("q", "kv", "sc", "w", "ks", "ke", "out"):
+        assert call(**{name: NULL}) == -1, name
+    assert call(S=0) == -2
+    assert call(S_kv=0) == -2
+    assert call(D=64) == -2 and call(D=256) == -2           # head dim 128 only
+    assert call(H=8) == -2 and call(H=80) == -2 and call(H=24) == -2
+    assert call(S_kv=1 << 24) == -2                         # S_kv * 128 reaches 2^31
+    assert call(q=MIS) == -3 and call(kv=MIS) == -3 and call(w=MIS) == -3
+    odd = ct.c_void_p(0x10002)
+    for name in ("sc", "ks", "ke", "out"):
+        assert call(**{name: odd}) == -3, name
