@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload decode|prefill|contiguous|masked|small|prefill_ue8m0|contiguous_ue8m0]
+                    [--workload decode|prefill|contiguous|masked|small|prefill_ue8m0|contiguous_ue8m0|mqa]
 
 A step is one pass of the hot path over one batch of synthetic input: for
 every GEMM of the workload, quantise the fp32 activations (1x128 scales) and
@@ -17,6 +17,10 @@ is re-read only after more than 512 MB of other traffic (the 256 MB
 Infinity Cache cannot serve it).  Per-kernel durations for the roofline are
 measured separately with HIP events around graph replays of one GEMM launch
 repeated over rotating weight copies.
+
+Workload mqa: one FP8 MQA logits call (the v3.2 indexer's scoring) of 4096
+query tokens x 64 heads against 8192 keys with causal ranges, inputs already
+E4M3 and resident; value -> TFLOP/s of 2 * H * 128 per computed logit.
 
 Prints ONE JSON line.  `value` is whole-job throughput: decode -> GB/s of
 algorithmic HBM traffic (activation read + codes/scales written by the
@@ -184,6 +188,27 @@ def masked_jobs():
 # timing
 # ---------------------------------------------------------------------------
 
+def mqa_jobs():
+    """One FP8 MQA logits call (the v3.2 indexer's scoring) over a causal
+    prefill chunk; inputs are already E4M3 (as the indexer holds them)."""
+    cfg = synth.MQA
+    S, S_kv, H, D = cfg["S"], cfg["S_kv"], cfg["H"], cfg["D"]
+    qn, kvn, scn, wn = synth.mqa_tensors(cfg["seed"], S, H, S_kv, D)
+    ksn, ken = synth.causal_ranges(S, S_kv)
+    q, kv, sc, w = (torch.from_numpy(x).cuda() for x in (qn, kvn, scn, wn))
+    ks, ke = torch.from_numpy(ksn).cuda(), torch.from_numpy(ken).cuda()
+    out = torch.empty((S, S_kv), dtype=torch.float32, device="cuda")
+
+    def launch(ci, with_quant):
+        dg.fp8_mqa_logits(q, kv, sc, w, ks, ke, True, logits=out)
+
+    pairs = int(np.sum(np.maximum(np.minimum(ken, S_kv) - np.maximum(ksn, 0), 0)))
+    flops = 2.0 * pairs * H * D
+    nbytes = S * H * D + S_kv * D + 4 * S_kv + 4 * S * H + 8 * S + 4 * S * S_kv
+    meta = {"S": S, "S_kv": S_kv, "H": H, "D": D, "pairs": pairs, "ranges": "causal, query i sees [0, S_kv-S+i+1)"}
+    return [Job(cfg["name"], launch, 1, flops, nbytes, 0)], meta
+
+
 _CAPTURE_STREAM = None
 
 
@@ -262,6 +287,8 @@ def measured_traffic(workload, jobs):
 def cpu_baseline(workload, jobs_meta, budget_s=15.0):
     import oracle
     cores = oracle.num_threads()
+    if workload == "mqa":
+        return cpu_baseline_mqa(jobs_meta, budget_s)
     if workload != "decode":
         return None
     total_bytes = 0
@@ -301,6 +328,30 @@ def cpu_baseline(workload, jobs_meta, budget_s=15.0):
             "seconds_full_step_extrapolated": t_full}
 
 
+def cpu_baseline_mqa(meta, budget_s):
+    import oracle
+    cfg = synth.MQA
+    S, S_kv, H, D = cfg["S"], cfg["S_kv"], cfg["H"], cfg["D"]
+    q, kv, sc, w = synth.mqa_tensors(cfg["seed"], S, H, S_kv, D)
+    ks, ke = synth.causal_ranges(S, S_kv)
+    lens = np.maximum(np.minimum(ke, S_kv) - np.maximum(ks, 0), 0)
+    probe = np.arange(S - oracle.num_threads(), S, dtype=np.int32)     # one row per thread
+    t0 = time.perf_counter()
+    oracle.mqa_logits_rows(q, kv, sc, w, ks, ke, True, probe)
+    rate = float(lens[probe].sum()) / (time.perf_counter() - t0)       # computed logits per second
+    n = int(min(S, max(8, budget_s * rate / float(lens.mean()))))
+    rows = np.unique(np.linspace(0, S - 1, n).round().astype(np.int32))
+    t0 = time.perf_counter()
+    oracle.mqa_logits_rows(q, kv, sc, w, ks, ke, True, rows)
+    t = time.perf_counter() - t0
+    t_full = t * float(lens.sum()) / float(lens[rows].sum())
+    flops = 2.0 * float(lens.sum()) * H * D
+    return {"value": flops / t_full / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"{rows.size} of {S} query rows, evenly spaced ({int(lens[rows].sum())} of "
+                       f"{int(lens.sum())} computed logits); time scaled to the whole call by that fraction"),
+            "seconds_full_step_extrapolated": t_full}
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -309,7 +360,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "contiguous", "masked", "small", "prefill_ue8m0", "contiguous_ue8m0"])
+                    choices=["decode", "prefill", "contiguous", "masked", "small", "prefill_ue8m0", "contiguous_ue8m0",
+                             "mqa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB each (reference for HBM byte counters)")
@@ -344,6 +396,9 @@ def main():
         bound = "mfma"
     elif args.workload == "contiguous_ue8m0":
         jobs, meta = contiguous_jobs(ue8m0=True)
+        bound = "mfma"
+    elif args.workload == "mqa":
+        jobs, meta = mqa_jobs()
         bound = "mfma"
     elif args.workload == "small":
         jobs = dense_jobs([synth.DENSE_SMALL])
@@ -420,6 +475,8 @@ def main():
                          "C bf16, bf16 D, power-of-two (UE8M0) block scales",
         "contiguous_ue8m0": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168, "
                             "power-of-two (UE8M0) block scales",
+        "mqa": "FP8 MQA logits (non-paged, clean_logits): 4096 query tokens x 64 heads x 128 against 8192 keys, "
+               "causal ranges, fp32 logits [4096, 8192]",
     }[args.workload]
     out = {
         "metric": METRIC,
@@ -433,9 +490,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3",
-        "data": "synthetic: seeded N(0,1) fp32, quantised to e4m3 with 1x128 / 128x128 fp32 scales"
-                + (" rounded up to powers of two (UE8M0)" if args.workload.endswith("_ue8m0") else ""),
-        "config": {"workload": workload_desc, "step": "activation quantiser + GEMM per shape; weights pre-quantised",
+        "data": ("synthetic: seeded uniformly random e4m3 codes for q and kv, kv_scale 2^-9 (1+U[0,1)), "
+                 "weights N(0,1)/8" if args.workload == "mqa" else
+                 "synthetic: seeded N(0,1) fp32, quantised to e4m3 with 1x128 / 128x128 fp32 scales"
+                 + (" rounded up to powers of two (UE8M0)" if args.workload.endswith("_ue8m0") else "")),
+        "config": {"workload": workload_desc,
+                   "step": ("one fp8_mqa_logits call, inputs resident" if args.workload == "mqa" else
+                            "activation quantiser + GEMM per shape; weights pre-quantised"),
                    "graph_replay": True, **({"layout": meta} if meta else {})},
         "roofline": roof,
         "cpu_baseline": cpu,

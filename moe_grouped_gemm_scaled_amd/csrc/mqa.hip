@@ -294,8 +294,8 @@ hipError_t launch_nt(const MqaParams &p, hipStream_t stream, std::string &config
     const long grid = (long)((k.n_qblk + 7) / 8) * 8 * k.n_chunk;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     char buf[160];
-    snprintf(buf, sizeof buf, "mqa_logits heads=%d queries/wg=%d chunk=%d keys stages=%d grid=%ld%s", 16 * NT,
-             4 * NQ, CH_STAGES * kStageKeys, NST, grid, k.vec ? "" : " scalar-stores");
+    snprintf(buf, sizeof buf, "family=mqa heads=%d queries/wg=%d chunk=%d stages=%d grid=%ld%s", 16 * NT, 4 * NQ,
+             CH_STAGES * kStageKeys, NST, grid, k.vec ? "" : " scalar-stores");
     config = buf;
     hipLaunchKernelGGL((mqa_kernel<NT, NQ, CH_STAGES, NST>), dim3((unsigned)grid), dim3(256), 0, stream, k);
     return hipGetLastError();

@@ -24,7 +24,7 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["dg_device.h", "dg_internal.h", "dg_pipeline.h", "gemm.hip", "decode.hip", "pipelined.hip",
+KERNEL_SOURCES = ["dg_device.h", "dg_internal.h", "dg_pipeline.h", "gemm.hip", "decode.hip", "pipelined.hip", "mqa.hip",
                   "persistent.hip", "quant.hip"]
 
 
@@ -97,6 +97,8 @@ def _kernel_fragment(config):
         bm, bn = kv["tile"].split("x")[:2]
         wm, wn = kv["waves"].split("x")
         frag = f"{fam}_kernel<{bm}, {bn}, {wm}, {wn}, {kv['stages']}, {kv['kblocks_per_stage']}, "
+    elif fam == "mqa":
+        frag = f"mqa_kernel<{int(kv['heads']) // 16}, "
     elif fam == "skinny":
         wm, wn = kv["waves"].split("x")
         frag = (f"skinny_kernel<{int(kv['rows']) // 16}, {int(kv['cols']) // 16}, {wm}, {wn}, {kv['ks']}, "
