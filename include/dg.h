@@ -72,6 +72,37 @@ int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa,
                    int M, int N, int K, void *stream);
 
 /*
+ * The other memory layouts of the dense GEMM ("DeepGEMM" README summary,
+ * sections "GEMM interface and layout constraints" and "Dense and Grouped
+ * GEMM": fp8_gemm_{nt, nn, tn, tt}, D = C + A @ B with each operand either
+ * as stored or transposed).  The product, the scales and their layouts are
+ * those of dg_fp8_gemm_nt:
+ *   D[m,n] = C[m,n] + sum_kb sfa[kb][m] * sfb[n/128][kb] * sum_{k in kb} A(m,k) B(n,k)
+ * only where A(m,k) and B(n,k) are stored differs:
+ *   nn: a [M][K] (A(m,k) = a[m*K + k]),  b [K][N] (B(n,k) = b[k*N + n])
+ *   tn: a [K][M] (A(m,k) = a[k*M + m]),  b [K][N]
+ *   tt: a [K][M],                        b [N][K] (as in nt)
+ * An operand stored [K][M] or [K][N] (MN-major) needs M (resp. N) a multiple
+ * of 16, so that its rows are 16-byte aligned, and K*M (K*N) below 2^31.
+ * Same arguments otherwise, same tolerance, same errors as dg_fp8_gemm_nt,
+ * plus DG_ERR_ALIGN (M or N of an MN-major operand not a multiple of 16) and
+ * DG_ERR_SHAPE (K*M or K*N reaching 2^31).  These always run on the
+ * pipelined kernel family, whatever dg_set_kernel_family selects.
+ */
+int dg_fp8_gemm_nn(const uint8_t *a, const float *sfa, int ld_sfa,
+                   const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d,
+                   int M, int N, int K, void *stream);
+int dg_fp8_gemm_tn(const uint8_t *a, const float *sfa, int ld_sfa,
+                   const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d,
+                   int M, int N, int K, void *stream);
+int dg_fp8_gemm_tt(const uint8_t *a, const float *sfa, int ld_sfa,
+                   const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d,
+                   int M, int N, int K, void *stream);
+
+/*
  * M-grouped contiguous layout ("DeepGEMM" README summary, section "Dense and
  * Grouped GEMM"): the tokens of all experts are concatenated along M, N and K
  * are shared, and every expert segment starts at a multiple of the M block

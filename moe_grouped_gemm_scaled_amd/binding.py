@@ -50,6 +50,12 @@ EXPORTS = {
                                                 ct.c_void_p, ct.c_int, ct.c_void_p]),
     "dg_quantize_e4m3_128x128_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
                                                   ct.c_void_p, ct.c_void_p]),
+    "dg_fp8_gemm_nn": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                  ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_fp8_gemm_tn": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                  ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_fp8_gemm_tt": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                  ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
     "dg_fp8_mqa_logits": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                      ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
                                      ct.c_void_p]),
@@ -139,6 +145,26 @@ def fp8_gemm_nt(a, sfa, b, sfb, d, c=None, ue8m0=False):
             _ptr(b, _FP8, "b", (N, K)), _ptr(sfb, torch.float32, "sfb", (ceil_div(N, 128), K // 128)),
             _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
     name = _name("dg_fp8_gemm_nt", ue8m0)
+    _check(getattr(lib(), name)(*args), name)
+    return d
+
+
+def fp8_gemm(layout, a, sfa, b, sfb, d, c=None):
+    """D = C + A @ B in one of the layouts "nt", "nn", "tn", "tt" (dg_fp8_gemm_<layout>).
+    The first letter is A's storage: "n" a[M,K], "t" a[K,M]; the second B's: "t" b[N,K], "n" b[K,N].
+    Scales as for fp8_gemm_nt: sfa[K/128, ld_sfa], sfb[ceil(N/128), K/128]; d/c[M,N] bf16."""
+    if layout not in ("nt", "nn", "tn", "tt"):
+        raise ValueError(f"layout {layout!r}")
+    M, N = d.shape
+    K = a.shape[1] if layout[0] == "n" else a.shape[0]
+    a_shape = (M, K) if layout[0] == "n" else (K, M)
+    b_shape = (N, K) if layout[1] == "t" else (K, N)
+    if sfa.dim() != 2 or sfa.shape[0] != K // 128:
+        raise ValueError(f"sfa: shape {tuple(sfa.shape)}, expected [K/128={K // 128}, ld_sfa]")
+    args = (_ptr(a, _FP8, "a", a_shape), _ptr(sfa, torch.float32, "sfa"), int(sfa.shape[1]),
+            _ptr(b, _FP8, "b", b_shape), _ptr(sfb, torch.float32, "sfb", (ceil_div(N, 128), K // 128)),
+            _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
+    name = "dg_fp8_gemm_" + layout
     _check(getattr(lib(), name)(*args), name)
     return d
 

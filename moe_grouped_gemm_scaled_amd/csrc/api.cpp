@@ -104,6 +104,40 @@ static int masked_impl(const uint8_t *a, const float *sfa, const uint8_t *b, con
     return run_gemm(p, stream);
 }
 
+// NN, TN and TT layouts: an MN-major operand needs 16-byte rows (M or N a
+// multiple of 16) and 32-bit buffer offsets (K * M, K * N below 2^31).
+static int gemm_layout_impl(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                            const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream, bool a_mn,
+                            bool b_mn) {
+    if (!a || !sfa || !b || !sfb || !d) return DG_ERR_NULL;
+    if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if ((int64_t)K * M >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31)) return DG_ERR_SHAPE;
+    if ((a_mn && M % 16 != 0) || (b_mn && N % 16 != 0)) return DG_ERR_ALIGN;
+    if (ld_sfa < M || ld_sfa % 4 != 0) return DG_ERR_ALIGN;
+    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+        (c && !aligned16(c)))
+        return DG_ERR_ALIGN;
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, false};
+    p.a_mn = a_mn;
+    p.b_mn = b_mn;
+    return run_gemm(p, stream);
+}
+
+int dg_fp8_gemm_nn(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false, true);
+}
+
+int dg_fp8_gemm_tn(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, true);
+}
+
+int dg_fp8_gemm_tt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                   const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, false);
+}
+
 int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                    const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
     return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false);

@@ -42,6 +42,9 @@ struct GemmProblem {
     // family then applies them in the MFMA itself; other families promote
     // in fp32 as usual, which is exact for such scales
     bool ue8m0 = false;
+    // dense only: A stored MN-major as [K][M] (TN, TT layouts), B as [K][N]
+    // (NN, TN); only the pipelined family takes these
+    bool a_mn = false, b_mn = false;
 };
 
 // Skinny-M family: dense with M <= 128, and the masked layout; needs K >= 256

@@ -296,6 +296,9 @@ std::atomic<int> &kernel_family_setting() {
 }
 
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
+    // MN-major operands (NN, TN, TT layouts): the pipelined family only,
+    // whatever the family setting
+    if (p.a_mn || p.b_mn) return launch_pipe(p, num_cus, stream, config);
     const int f = kernel_family_setting().load(std::memory_order_relaxed);
     if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
     if (f == 2 && pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);

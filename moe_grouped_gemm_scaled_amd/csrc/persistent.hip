@@ -599,7 +599,7 @@ persist_kernel(PersistParams p) {
     auto dma = [&](uint8_t *stg) __attribute__((always_inline)) {
         const int kb = p_s * KS;
         dma_step<DA, DB, RG_STEP * 1024, RG_STEP * 1024>(stg, rA, rB, rS, va, vb, v_s, lds_a, lds_b, lds_s,
-                                                         kb * kKBlock, kb * s_stride);
+                                                         kb * kKBlock, kb * kKBlock, kb * s_stride);
     };
 
     // ---- main loop.  Every stage starts as "nothing to multiply"; round r,

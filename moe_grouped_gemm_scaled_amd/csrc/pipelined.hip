@@ -60,6 +60,8 @@ struct PipeParams {
     // split-K: tiles [0, split_hi) have splits_lo + 1 splits, the others
     // splits_lo; `slots` = partial slots per tile in `ws`
     int splits_lo, split_hi, slots;
+    // row pitch (bytes) of an operand stored MN-major: A as [K][lda], B as [K][ldb]
+    int lda, ldb;
 };
 
 // Contiguous layout with 256-row tiles: the u-th "unit" of 256 rows.  Units
@@ -111,7 +113,11 @@ __device__ __forceinline__ int contig_unit_block(const int32_t *idx, int nblocks
     return -1;
 }
 
-template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false>
+// AMN / BMN: A (B) is stored MN-major, as [K][M] ([K][N]); its LDS tiles
+// then hold K rows of BM (BN) bytes and fragments are read with transposing
+// LDS loads (read_frag_tr).
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false,
+          bool AMN = false, bool BMN = false>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 pipe_kernel(PipeParams p) {
     constexpr int NW = WGM * WGN;
@@ -138,6 +144,9 @@ pipe_kernel(PipeParams p) {
     static_assert(BM / 4 <= 64 && NBW <= 64, "one scale DMA per wave per K block");
     static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns share one scale block");
     static_assert(TM % EPI_ROWS == 0 && (TN % 8) == 0, "epilogue chunks");
+    static_assert((!AMN || (BM == 128 || BM == 256)) && (!BMN || (BN == 128 || BN == 256)),
+                  "MN-major tiles: K rows of 8 or 16 swizzled 16-byte columns, 1-KB DMA chunks of whole rows");
+    static_assert(!(AMN || BMN) || (MODE == Mode::Dense && !UE), "MN-major operands: dense layout, fp32 scales");
     static_assert(NW % 2 == 0 && (NW / 2) * EPI_ROWS * EPI_PITCH * 4 <= STAGE,
                   "epilogue staging: half the waves per stage");
 
@@ -260,13 +269,30 @@ pipe_kernel(PipeParams p) {
     const int wk = wave % KS, wr = wave / KS;      // K block and first row group of this wave's chunks
     constexpr int RG_STEP = NW / KS;               // row groups between a wave's chunks
     int va[DA], vb[DB];
+    // MN-major operand: chunk c holds K rows RPC*(c / KS) .. +RPC-1 of K
+    // block c % KS (RPC = 1024 / BM rows of BM bytes); lane l lands at row
+    // +l/CPR, 16-byte column l%CPR and fetches column (l%CPR) ^ (row & 7).
+    // Columns past M (N) clamp to the row's last 16 bytes (M and N are
+    // multiples of 16 here); their products are never stored.
     static_for<DA>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
-        va[i] = min(m0 + 8 * (wr + RG_STEP * i) + (lane >> 3), rows_a - 1) * K + wk * kKBlock + dchunk;
+        if constexpr (AMN) {
+            constexpr int CPR = BM / 16, RPC = 1024 / BM;
+            const int krow = RPC * (wr + RG_STEP * i) + lane / CPR;
+            va[i] = (wk * kKBlock + krow) * p.lda + min(m0 + 16 * ((lane % CPR) ^ (krow & 7)), p.lda - 16);
+        } else {
+            va[i] = min(m0 + 8 * (wr + RG_STEP * i) + (lane >> 3), rows_a - 1) * K + wk * kKBlock + dchunk;
+        }
     });
     static_for<DB>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
-        vb[i] = min(n0 + 8 * (wr + RG_STEP * i) + (lane >> 3), N - 1) * K + wk * kKBlock + dchunk;
+        if constexpr (BMN) {
+            constexpr int CPR = BN / 16, RPC = 1024 / BN;
+            const int krow = RPC * (wr + RG_STEP * i) + lane / CPR;
+            vb[i] = (wk * kKBlock + krow) * p.ldb + min(n0 + 16 * ((lane % CPR) ^ (krow & 7)), p.ldb - 16);
+        } else {
+            vb[i] = min(n0 + 8 * (wr + RG_STEP * i) + (lane >> 3), N - 1) * K + wk * kKBlock + dchunk;
+        }
     });
     const int lds_a = wk * BLK_A + wr * 1024;
     const int lds_b = OFF_B + wk * BLK_B + wr * 1024;
@@ -287,7 +313,8 @@ pipe_kernel(PipeParams p) {
     auto dma = [&](uint8_t *stg, int st) __attribute__((always_inline)) {
         const int kb = st * KS;
         dma_step<DA, DB, RG_STEP * 1024, RG_STEP * 1024>(stg, rA, rB, rS, va, vb, v_s, lds_a, lds_b, lds_s,
-                                                         kb * kKBlock, kb * s_stride);
+                                                         AMN ? kb * kKBlock * p.lda : kb * kKBlock,
+                                                         BMN ? kb * kKBlock * p.ldb : kb * kKBlock, kb * s_stride);
     };
 
     v4f acc[SM][SN];
@@ -316,6 +343,26 @@ pipe_kernel(PipeParams p) {
         off_sa0 = opaque_offset(OFF_SA + rowa * 4);
     }
     const int off_sb = OFF_SB + 16 * wave_nb;
+    // MN-major fragments: lane l of group g = l/16 addresses K row
+    // 16g + (l%16)/2 and columns +8*(l & 1) of the 16-column subtile; the
+    // swizzle (row & 7) = (l%16)/2 is fixed per lane, so each subtile gets its
+    // own base offset
+    int off_amn[AMN ? SM : 1], off_bmn[BMN ? SN : 1];
+    if constexpr (AMN) {
+        static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            const int c = (wm * TM) / 16 + i;
+            off_amn[i] = opaque_offset((16 * g4 + (l16 >> 1)) * BM + ((c ^ ((l16 >> 1) & 7)) << 4) + 8 * (l16 & 1));
+        });
+    }
+    if constexpr (BMN) {
+        static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            const int c = (wn * TN) / 16 + j;
+            off_bmn[j] = opaque_offset(OFF_B + (16 * g4 + (l16 >> 1)) * BN + ((c ^ ((l16 >> 1) & 7)) << 4) +
+                                       8 * (l16 & 1));
+        });
+    }
 
     // Multiply K block kk of the step held in `stg`.  The MFMA takes the B
     // fragment as its first operand, so it yields the transposed block
@@ -333,15 +380,23 @@ pipe_kernel(PipeParams p) {
         v8i bf[SN];
         static_for<SN>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b0[0] + j * 16 * kKBlock);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b0[1] + j * 16 * kKBlock);
-            bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (BMN) {
+                bf[j] = read_frag_tr<BN>(stg_b + off_bmn[j]);
+            } else {
+                const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b0[0] + j * 16 * kKBlock);
+                const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b0[1] + j * 16 * kKBlock);
+                bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
         });
         auto read_a = [&](auto ic, v8i &af, float &sa) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a0[0] + i * 16 * kKBlock);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
-            af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (AMN) {
+                af = read_frag_tr<BM>(stg + off_amn[i]);
+            } else {
+                const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a0[0] + i * 16 * kKBlock);
+                const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
+                af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
             sa = *reinterpret_cast<const float *>(stg_s + off_sa0 + i * 64);
         };
         v8i af_cur, af_nxt;
@@ -418,9 +473,13 @@ pipe_kernel(PipeParams p) {
         v8i bf[SN];
         static_for<SN>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b0[0] + j * 16 * kKBlock);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b0[1] + j * 16 * kKBlock);
-            bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (BMN) {
+                bf[j] = read_frag_tr<BN>(stg_b + off_bmn[j]);
+            } else {
+                const v4i lo = *reinterpret_cast<const v4i *>(stg_b + off_b0[0] + j * 16 * kKBlock);
+                const v4i hi = *reinterpret_cast<const v4i *>(stg_b + off_b0[1] + j * 16 * kKBlock);
+                bf[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
         });
         static_for<SM>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
@@ -586,11 +645,14 @@ bool pipe_eligible(const GemmProblem &p) {
 // split over about units/tiles workgroups (some tiles one more than others,
 // so that exactly `units` workgroups run), each split keeping at least one
 // step; otherwise, or when no workspace is available, there is no split.
-template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false>
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false,
+          bool AMN = false, bool BMN = false>
 hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, std::string &config) {
     PipeParams k;
     k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.d = p.d; k.idx = p.idx;
     k.rows_a = p.rows_a; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.G = p.G;
+    k.lda = p.rows_a;
+    k.ldb = p.N;
     k.tiles_m = (p.rows_a + BM - 1) / BM;
     if (MODE == Mode::Contig && BM == 256) {
         // units: at most one per 256 rows plus one per expert segment
@@ -633,19 +695,20 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
     char buf[220];
     snprintf(buf, sizeof buf,
              "family=pipe mode=%d tile=%dx%dx128 waves=%dx%d stages=%d kblocks_per_stage=%d deep=%d splits=%d%s "
-             "grid=%lld%s",
+             "grid=%lld%s%s",
              (int)MODE, BM, BN, WGM, WGN, NST, KS, (int)DEEP, split ? k.splits_lo : 1,
-             split && k.split_hi > 0 ? "+" : "", (long long)grid, UE ? " scales=ue8m0" : "");
+             split && k.split_hi > 0 ? "+" : "", (long long)grid, UE ? " scales=ue8m0" : "",
+             AMN ? (BMN ? " layout=tn" : " layout=tt") : (BMN ? " layout=nn" : ""));
     config = buf;
     if constexpr (SPLIT) {
         if (split) {
-            hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true, UE>), dim3((unsigned)grid),
-                               dim3(64 * WGM * WGN), 0, stream, k);
+            hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true, UE, AMN, BMN>),
+                               dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, stream, k);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, false, UE>), dim3((unsigned)grid),
-                           dim3(64 * WGM * WGN), 0, stream, k);
+    hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, false, UE, AMN, BMN>),
+                       dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, stream, k);
     return hipGetLastError();
 }
 
@@ -697,8 +760,27 @@ static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t 
     return hipErrorInvalidValue;
 }
 
+// Dense GEMMs with an operand stored MN-major (the NN, TN and TT layouts):
+// the prefill tiles of the NT path (256x256 for long K or a whole number of
+// waves of tiles, 128x128 otherwise), without split-K.
+template <bool AMN, bool BMN>
+static hipError_t launch_pipe_layout(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int nkb = p.K / kKBlock;
+    const int64_t t256 = (int64_t)((p.rows_a + 255) / 256) * ((p.N + 255) / 256);
+    if (p.rows_a >= 256 && (nkb > 16 || t256 % cus == 0))
+        return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, false, AMN, BMN>(p, 0, stream, config);
+    return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, false, AMN, BMN>(p, 0, stream, config);
+}
+
 hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     if (!pipe_eligible(p)) return hipErrorInvalidValue;
+    if (p.a_mn || p.b_mn) {
+        if (p.mode != Mode::Dense || p.ue8m0) return hipErrorInvalidValue;
+        if (p.a_mn && p.b_mn) return launch_pipe_layout<true, true>(p, num_cus, stream, config);
+        if (p.a_mn) return launch_pipe_layout<true, false>(p, num_cus, stream, config);
+        return launch_pipe_layout<false, true>(p, num_cus, stream, config);
+    }
     return p.ue8m0 ? launch_pipe_ue<true>(p, num_cus, stream, config) : launch_pipe_ue<false>(p, num_cus, stream, config);
 }
 

@@ -169,6 +169,29 @@ def gemm_nt_at(a, sfa, b, sfb, c, ms, ns):
     return out
 
 
+def _logical(layout, a, b):
+    """The stored operands of layout nt/nn/tn/tt as the logical A[M,K] and B[N,K]
+    (GeekNews summary of the DeepGEMM README, layout section: the first letter
+    tells whether A is stored as is ("n", [M,K]) or transposed ("t", [K,M]); the
+    second whether B is stored transposed ("t", [N,K]) or as is ("n", [K,N]))."""
+    if layout not in ("nt", "nn", "tn", "tt"):
+        raise ValueError(layout)
+    a_l = _np.ascontiguousarray(a if layout[0] == "n" else _np.asarray(a).T)
+    b_l = _np.ascontiguousarray(b if layout[1] == "t" else _np.asarray(b).T)
+    return a_l, b_l
+
+
+def gemm_layout(layout, a, sfa, b, sfb, c=None):
+    """D = C + A @ B for a stored layout: the NT definition on the logical operands."""
+    a_l, b_l = _logical(layout, a, b)
+    return gemm_nt(a_l, sfa, b_l, sfb, c)
+
+
+def gemm_layout_at(layout, a, sfa, b, sfb, c, ms, ns):
+    a_l, b_l = _logical(layout, a, b)
+    return gemm_nt_at(a_l, sfa, b_l, sfb, c, ms, ns)
+
+
 def m_grouped_contiguous(a, sfa, b, sfb, c, m_indices, d=None):
     """a[M_total,K], sfa[K/128, M_total], b[G,N,K], sfb[G, ceil(N/128), K/128], m_indices[M_total]."""
     M_total, K = a.shape

@@ -146,3 +146,20 @@ def test_mqa_logits_argument_errors(lib):
     odd = ct.c_void_p(0x10002)
     for name in ("sc", "ks", "ke", "out"):
         assert call(**{name: odd}) == -3, name
+
+
+def test_layout_argument_errors(lib):
+    # a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream
+    for name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+        f = getattr(lib, name)
+        assert f(NULL, P, 64, P, P, NULL, P, 64, 64, 128, S) == -1, name
+        assert f(P, P, 64, P, P, NULL, P, 64, 64, 100, S) == -2, name        # K % 128
+        assert f(P, P, 64, P, P, NULL, P, 0, 64, 128, S) == -2, name
+        assert f(P, P, 60, P, P, NULL, P, 64, 64, 128, S) == -3, name        # ld_sfa < M
+        assert f(MIS, P, 64, P, P, NULL, P, 64, 64, 128, S) == -3, name
+        assert f(P, P, 1 << 20, P, P, NULL, P, 1 << 20, 64, 4096, S) == -2, name   # K * M reaches 2^31
+    # an MN-major operand needs 16-byte rows
+    assert lib.dg_fp8_gemm_tn(P, P, 72, P, P, NULL, P, 72, 64, 128, S) == -3      # M % 16
+    assert lib.dg_fp8_gemm_tn(P, P, 64, P, P, NULL, P, 64, 72, 128, S) == -3      # N % 16
+    assert lib.dg_fp8_gemm_tt(P, P, 72, P, P, NULL, P, 72, 64, 128, S) == -3      # M % 16
+    assert lib.dg_fp8_gemm_nn(P, P, 64, P, P, NULL, P, 64, 72, 128, S) == -3      # N % 16

@@ -336,6 +336,29 @@ def test_gemm_equals_matmul_of_descaled_operands(M, N, K, with_c):
     assert np.all(np.abs(d - ref) <= mag * 2.0 ** -48)
 
 
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+@pytest.mark.parametrize("M,N,K", [(48, 160, 256), (128, 96, 128)])
+def test_gemm_layouts_equal_matmul_in_the_stated_orientation(layout, M, N, K):
+    """D = C + A @ B in each stored layout (nn: a[M,K], b[K,N]; tn: a[K,M],
+    b[K,N]; tt: a[K,M], b[N,K]): numpy matmul of the de-scaled operands taken
+    in the orientation the layout names (a.T where A is stored [K,M], b where
+    B is stored [K,N]).  M == K in one case, so that reading a stored [K,M]
+    as [M,K] would go unnoticed by the shapes alone."""
+    a, sfa, b, sfb, c = _random_problem(M, N, K, seed=M + N + K + len(layout))
+    a_st = np.ascontiguousarray(a.T) if layout[0] == "t" else a
+    b_st = np.ascontiguousarray(b.T) if layout[1] == "n" else b
+    d = oracle.gemm_layout(layout, a_st, sfa, b_st, sfb, c)
+    SA, SB = _expand_scales(sfa, sfb, M, N, K)
+    A_mk = (torch_decode(a_st).T if layout[0] == "t" else torch_decode(a_st)) * SA       # [M, K]
+    B_kn = (torch_decode(b_st) if layout[1] == "n" else torch_decode(b_st).T) * SB.T     # [K, N]
+    ref = A_mk @ B_kn + synth.bf16_bits_to_f32(c).astype(np.float64)
+    mag = np.abs(A_mk) @ np.abs(B_kn) + np.abs(synth.bf16_bits_to_f32(c))
+    assert np.all(np.abs(d - ref) <= mag * 2.0 ** -48)
+    ms = np.array([0, M - 1, M // 2], np.int32)
+    ns = np.array([N - 1, 0, N // 3], np.int32)
+    assert np.array_equal(oracle.gemm_layout_at(layout, a_st, sfa, b_st, sfb, c, ms, ns), d[ms, ns])
+
+
 def test_gemm_single_block_unit_scales_is_exact_matmul():
     M, N, K = 19, 23, 128
     a = synth.random_codes(31, 0, (M, K))
