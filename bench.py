@@ -1,7 +1,8 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload decode|prefill|contiguous|masked|small|prefill_ue8m0|contiguous_ue8m0|mqa]
+                    [--workload decode|prefill|contiguous|masked|small|prefill_ue8m0|contiguous_ue8m0|mqa|
+                                prefill_nn|prefill_tn|prefill_tt]
 
 A step is one pass of the hot path over one batch of synthetic input: for
 every GEMM of the workload, quantise the fp32 activations (1x128 scales) and
@@ -105,7 +106,10 @@ def replicate(t, n):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
-def dense_jobs(cfgs, ue8m0=False):
+def dense_jobs(cfgs, ue8m0=False, layout="nt"):
+    """layout "nt": activation quantiser + GEMM per shape.  Other layouts: the
+    GEMM alone, on operands quantised and stored in that layout beforehand
+    (A as [K, M] for tn/tt, B as [K, N] for nn/tn)."""
     jobs = []
     weights = {}
     for cfg in cfgs:
@@ -113,8 +117,9 @@ def dense_jobs(cfgs, ue8m0=False):
         key = (M, N, K)           # no sharing between jobs: every GEMM streams its own copies
         if key not in weights:
             b, sfb = make_weights(1, N, K, seed, ue8m0)
+            b0 = b[0] if layout[1] == "t" else b[0].t().contiguous()
             nc = n_copies(N * K)
-            weights[key] = (replicate(b[0], nc), replicate(sfb[0], nc))
+            weights[key] = (replicate(b0, nc), replicate(sfb[0], nc))
         bs, sfbs = weights[key]
         x = torch.from_numpy(synth.normal_f32(seed, synth.STREAM_A, (M, K))).cuda()
         a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
@@ -125,13 +130,23 @@ def dense_jobs(cfgs, ue8m0=False):
             c = c.view(torch.bfloat16)
         d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
-        def launch(ci, with_quant, x=x, a=a, sfa=sfa, bs=bs, sfbs=sfbs, c=c, d=d):
-            if with_quant:
-                dg.quantize_e4m3_1x128(x, q=a, sf=sfa, ue8m0=ue8m0)
-            dg.fp8_gemm_nt(a, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c, ue8m0=ue8m0)
+        if layout == "nt":
+            def launch(ci, with_quant, x=x, a=a, sfa=sfa, bs=bs, sfbs=sfbs, c=c, d=d):
+                if with_quant:
+                    dg.quantize_e4m3_1x128(x, q=a, sf=sfa, ue8m0=ue8m0)
+                dg.fp8_gemm_nt(a, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c, ue8m0=ue8m0)
+            qbytes = quant_bytes(M, K)
+        else:
+            dg.quantize_e4m3_1x128(x, q=a, sf=sfa)
+            a_st = a if layout[0] == "n" else a.t().contiguous()
+            torch.cuda.synchronize()
+
+            def launch(ci, with_quant, a_st=a_st, sfa=sfa, bs=bs, sfbs=sfbs, c=c, d=d):
+                dg.fp8_gemm(layout, a_st, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c)
+            qbytes = 0
 
         jobs.append(Job(cfg["name"], launch, len(bs), 2.0 * M * N * K,
-                        gemm_bytes(M, N, K, with_c=cfg["with_c"]), quant_bytes(M, K)))
+                        gemm_bytes(M, N, K, with_c=cfg["with_c"]), qbytes))
     return jobs
 
 
@@ -361,7 +376,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "contiguous", "masked", "small", "prefill_ue8m0", "contiguous_ue8m0",
-                             "mqa"])
+                             "mqa", "prefill_nn", "prefill_tn", "prefill_tt"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB each (reference for HBM byte counters)")
@@ -396,6 +411,9 @@ def main():
         bound = "mfma"
     elif args.workload == "contiguous_ue8m0":
         jobs, meta = contiguous_jobs(ue8m0=True)
+        bound = "mfma"
+    elif args.workload in ("prefill_nn", "prefill_tn", "prefill_tt"):
+        jobs = dense_jobs(synth.PREFILL, layout=args.workload[-2:])
         bound = "mfma"
     elif args.workload == "mqa":
         jobs, meta = mqa_jobs()
@@ -475,6 +493,12 @@ def main():
                          "C bf16, bf16 D, power-of-two (UE8M0) block scales",
         "contiguous_ue8m0": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168, "
                             "power-of-two (UE8M0) block scales",
+        "prefill_nn": "prefill-shaped dense FP8 GEMM in the NN layout (A [M,K], B stored [K,N]), M=4096 x (N,K) in "
+                      "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
+        "prefill_tn": "prefill-shaped dense FP8 GEMM in the TN layout (A stored [K,M], B stored [K,N]), M=4096 x (N,K) in "
+                      "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
+        "prefill_tt": "prefill-shaped dense FP8 GEMM in the TT layout (A stored [K,M], B [N,K]), M=4096 x (N,K) in "
+                      "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
         "mqa": "FP8 MQA logits (non-paged, clean_logits): 4096 query tokens x 64 heads x 128 against 8192 keys, "
                "causal ranges, fp32 logits [4096, 8192]",
     }[args.workload]
@@ -496,6 +520,8 @@ def main():
                  + (" rounded up to powers of two (UE8M0)" if args.workload.endswith("_ue8m0") else "")),
         "config": {"workload": workload_desc,
                    "step": ("one fp8_mqa_logits call, inputs resident" if args.workload == "mqa" else
+                            "one GEMM per shape, operands quantised and laid out beforehand"
+                            if args.workload[-3:] in ("_nn", "_tn", "_tt") else
                             "activation quantiser + GEMM per shape; weights pre-quantised"),
                    "graph_replay": True, **({"layout": meta} if meta else {})},
         "roofline": roof,
