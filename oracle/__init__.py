@@ -49,6 +49,8 @@ def _load():
         "orc_m_grouped_contiguous_at": (None, [P, P, P, P, P, P, I, I, I, I, P, P, L, P]),
         "orc_m_grouped_masked": (None, [P, P, P, P, P, P, P, I, I, I, I]),
         "orc_m_grouped_masked_at": (None, [P, P, P, P, P, P, I, I, I, I, P, P, P, L, P]),
+        "orc_k_grouped_tn": (None, [P, P, P, P, P, P, I, I, I, P]),
+        "orc_k_grouped_tn_at": (None, [P, P, P, P, P, P, I, I, I, P, P, P, L, P]),
         "orc_mqa_logits": (None, [P, P, P, P, P, P, I, I, I, I, I, P]),
         "orc_mqa_logits_rows": (None, [P, P, P, P, P, P, I, I, I, I, P, I, P]),
         "orc_num_threads": (I, []),
@@ -244,6 +246,46 @@ def m_grouped_masked_at(a, sfa, b, sfb, c, masked_m, gs, ms, ns):
                                     _p(masked_m, _np.int32), G, M_cap, N, K,
                                     gs.ctypes.data, ms.ctypes.data, ns.ctypes.data, ms.size,
                                     out.ctypes.data)
+    return out
+
+
+def _kg_args(a, sfa, b, sfb, ks, c):
+    a = _np.ascontiguousarray(a, dtype=_np.uint8)
+    b = _np.ascontiguousarray(b, dtype=_np.uint8)
+    sfa = _np.ascontiguousarray(sfa, dtype=_np.float32)
+    sfb = _np.ascontiguousarray(sfb, dtype=_np.float32)
+    ks = _np.ascontiguousarray(ks, dtype=_np.int32)
+    K, M = a.shape
+    N = b.shape[1]
+    assert b.shape[0] == K and sfa.shape == (K // 128, M) and sfb.shape == (K // 128, N)
+    assert int(ks.sum()) <= K and _np.all(ks >= 0) and _np.all(ks % 128 == 0)
+    G = ks.size
+    cp = None
+    if c is not None:
+        c = _np.ascontiguousarray(c, dtype=_np.float32)
+        assert c.shape == (G, M, N)
+        cp = c.ctypes.data
+    return a, sfa, b, sfb, ks, c, cp, G, M, N
+
+
+def k_grouped_tn(a, sfa, b, sfb, ks, c=None):
+    """K-grouped TN contiguous GEMM: a[K,M], b[K,N] E4M3, sfa[K/128,M], sfb[K/128,N],
+    ks[G] group sizes (multiples of 128), c[G,M,N] fp32 or None -> d[G,M,N] fp64."""
+    a, sfa, b, sfb, ks, c, cp, G, M, N = _kg_args(a, sfa, b, sfb, ks, c)
+    d = _np.full((G, M, N), _np.nan, dtype=_np.float64)
+    _load().orc_k_grouped_tn(a.ctypes.data, sfa.ctypes.data, b.ctypes.data, sfb.ctypes.data, ks.ctypes.data, cp,
+                             G, M, N, d.ctypes.data)
+    return d
+
+
+def k_grouped_tn_at(a, sfa, b, sfb, ks, c, gs, ms, ns):
+    a, sfa, b, sfb, ks, c, cp, G, M, N = _kg_args(a, sfa, b, sfb, ks, c)
+    gs = _np.ascontiguousarray(gs, dtype=_np.int32)
+    ms = _np.ascontiguousarray(ms, dtype=_np.int32)
+    ns = _np.ascontiguousarray(ns, dtype=_np.int32)
+    out = _np.empty(gs.size, dtype=_np.float64)
+    _load().orc_k_grouped_tn_at(a.ctypes.data, sfa.ctypes.data, b.ctypes.data, sfb.ctypes.data, ks.ctypes.data, cp,
+                                G, M, N, gs.ctypes.data, ms.ctypes.data, ns.ctypes.data, gs.size, out.ctypes.data)
     return out
 
 

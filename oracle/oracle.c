@@ -381,6 +381,59 @@ void orc_m_grouped_masked_at(const uint8_t *a, const float *sfa,
 }
 
 /* ---------------------------------------------------------------------- */
+/* K-grouped GEMM, TN contiguous layout (MoE weight gradient; GeekNews     */
+/* summary of the DeepGEMM README, "Dense and Grouped GEMM": groups along  */
+/* K, M and N fixed, k_grouped_fp8_gemm_tn_contiguous).  The K rows of all */
+/* groups are concatenated: group g owns rows [k0_g, k0_g + ks[g]) of      */
+/* a [K][M] and b [K][N] (both stored with K as the slow index), ks[g] a    */
+/* multiple of 128.  Both operands carry one fp32 scale per 128 K rows and */
+/* per column: sfa[kb][m], sfb[kb][n].  For every group, also an empty one:*/
+/*   d[g][m][n] = c[g][m][n] + sum_{kb in g} sfa[kb][m] sfb[kb][n]          */
+/*                 * sum_{k in kb} A[k][m] B[k][n]                          */
+/* with exact block sums in fp64, K order.  c is fp32 [G][M][N] or NULL.   */
+/* ---------------------------------------------------------------------- */
+
+static double kgrouped_elem(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                            const int32_t *ks, const float *c, int G, int M, int N, int g, int m, int n)
+{
+    int k0 = 0;
+    for (int h = 0; h < g; ++h)
+        k0 += ks[h];
+    double acc = 0.0;
+    for (int kb = k0 / 128; kb < (k0 + ks[g]) / 128; ++kb) {
+        double p = 0.0;
+        for (int k = kb * 128; k < kb * 128 + 128; ++k)
+            p += T[a[(size_t)k * M + m]] * T[b[(size_t)k * N + n]];
+        acc += p * ((double)sfa[(size_t)kb * M + m] * (double)sfb[(size_t)kb * N + n]);
+    }
+    (void)G;
+    if (c)
+        acc += (double)c[((size_t)g * M + m) * N + n];
+    return acc;
+}
+
+void orc_k_grouped_tn(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                      const int32_t *ks, const float *c, int G, int M, int N, double *d)
+{
+    table_init();
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int g = 0; g < G; ++g)
+        for (int m = 0; m < M; ++m)
+            for (int n = 0; n < N; ++n)
+                d[((size_t)g * M + m) * N + n] = kgrouped_elem(a, sfa, b, sfb, ks, c, G, M, N, g, m, n);
+}
+
+void orc_k_grouped_tn_at(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                         const int32_t *ks, const float *c, int G, int M, int N, const int32_t *gs,
+                         const int32_t *ms, const int32_t *ns, int64_t count, double *out)
+{
+    table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = kgrouped_elem(a, sfa, b, sfb, ks, c, G, M, N, gs[i], ms[i], ns[i]);
+}
+
+/* ---------------------------------------------------------------------- */
 /* FP8 MQA logits (the DeepSeek v3.2 indexer's scoring kernel; GeekNews   */
 /* summary of the DeepGEMM README, ja.news.hada.io topic 19459, section on */
 /* the MQA kernels for the v3.2 Indexer, non-paged form).  For query token */

@@ -1,6 +1,7 @@
 /*
  * oracle.h -- plain CPU reference for the FP8 block-scaled NT GEMM, its
- * M-grouped variants, the E4M3 quantisers and the FP8 MQA logits.
+ * M-grouped variants, the K-grouped TN form, the E4M3 quantisers and the
+ * FP8 MQA logits.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
@@ -14,6 +15,8 @@
  *  - same page, section "Dense and Grouped GEMM": M-grouped contiguous layout
  *    (expert segments aligned to the M block) and masked layout (only the
  *    valid rows of each group are computed).
+ *  - same page, section "Dense and Grouped GEMM": the K-grouped API for the
+ *    MoE weight backward (M and N fixed, groups along K).
  *  - same page, section on the MQA kernels for the DeepSeek v3.2 Indexer:
  *    the non-paged fp8_mqa_logits inputs, shapes and per-token formula.
  *  - "DeepSeek open-sources DeepGEMM" news (picoinsstore.com), paragraph on
@@ -135,6 +138,19 @@ void orc_m_grouped_masked_at(const uint8_t *a, const float *sfa,
                              int G, int M_cap, int N, int K,
                              const int32_t *gs, const int32_t *ms,
                              const int32_t *ns, int64_t count, double *out);
+
+/* K-grouped TN contiguous GEMM (MoE weight gradient; GeekNews summary of
+ * the DeepGEMM README, "Dense and Grouped GEMM"): a [K][M], b [K][N] E4M3
+ * with the K rows of G groups concatenated (group g: ks[g] rows, a multiple
+ * of 128), scales sfa [K/128][M] and sfb [K/128][N] fp32, c fp32 [G][M][N]
+ * or NULL; d [G][M][N] fp64:
+ *   d[g][m][n] = c[g][m][n] + sum_{kb in g} sfa[kb][m] sfb[kb][n] sum_{k in kb} A[k][m] B[k][n].
+ * The _at form evaluates the listed (g, m, n) elements. */
+void orc_k_grouped_tn(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                      const int32_t *ks, const float *c, int G, int M, int N, double *d);
+void orc_k_grouped_tn_at(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                         const int32_t *ks, const float *c, int G, int M, int N, const int32_t *gs,
+                         const int32_t *ms, const int32_t *ns, int64_t count, double *out);
 
 /* FP8 MQA logits, non-paged (GeekNews summary of the DeepGEMM README, section
  * on the MQA kernels for the DeepSeek v3.2 Indexer):

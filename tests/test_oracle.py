@@ -639,3 +639,71 @@ def test_mqa_logits_ranges_clamped_and_rows_form_agrees():
         rows = np.array([6, 0, 3, 3], np.int32)
         sub = oracle.mqa_logits_rows(q, kv, kv_scale, weights, ks, ke, clean, rows)
         assert np.array_equal(sub, got[rows], equal_nan=True)
+
+
+# ---------------------------------------------------------------- K-grouped TN
+# MoE weight gradient (GeekNews summary of the DeepGEMM README, "Dense and
+# Grouped GEMM": groups along K, M and N fixed): d[g] = c[g] + A_g^T B_g with
+# A_g, B_g the K rows of group g, one scale per 128 K rows and per column.
+
+
+def _kg_problem(seed, ks, M, N, with_c=True):
+    K = int(np.sum(ks))
+    a = synth.random_codes(seed, 0, (K, M))
+    b = synth.random_codes(seed, 1, (K, N))
+    sfa = (synth.uniform(seed, 4, (K // 128) * M).reshape(K // 128, M) * 4 + 0.01).astype(np.float32)
+    sfb = (synth.uniform(seed, 5, (K // 128) * N).reshape(K // 128, N) * 4 + 0.01).astype(np.float32)
+    c = synth.normal_f32(seed, 2, (len(ks), M, N)) if with_c else None
+    return a, sfa, b, sfb, np.asarray(ks, np.int32), c
+
+
+def test_k_grouped_equals_per_group_matmul_of_descaled_operands():
+    ks = [256, 0, 128, 384]
+    M, N = 40, 72
+    a, sfa, b, sfb, ks, c = _kg_problem(70, ks, M, N)
+    d = oracle.k_grouped_tn(a, sfa, b, sfb, ks, c)
+    Ad = torch_decode(a) * np.repeat(sfa.astype(np.float64), 128, axis=0)       # [K, M]
+    Bd = torch_decode(b) * np.repeat(sfb.astype(np.float64), 128, axis=0)       # [K, N]
+    k0 = 0
+    for g, kg in enumerate(ks):
+        ref = Ad[k0:k0 + kg].T @ Bd[k0:k0 + kg] + c[g]
+        mag = np.abs(Ad[k0:k0 + kg]).T @ np.abs(Bd[k0:k0 + kg]) + np.abs(c[g])
+        assert np.all(np.abs(d[g] - ref) <= mag * 2.0 ** -48), g
+        k0 += kg
+    assert np.array_equal(d[1], c[1].astype(np.float64))            # empty group: D = C exactly
+
+
+def test_k_grouped_reduces_to_the_nt_gemm_with_block_constant_column_scales():
+    """With sfb constant over each 128 columns, group g is the NT GEMM of the
+    transposed group rows with 128x128 B scales: same block sums, same order,
+    so the two oracle functions agree bit for bit."""
+    ks = [128, 256, 384]
+    M, N = 24, 200
+    a, sfa, b, sfb, ks, _ = _kg_problem(71, ks, M, N, with_c=False)
+    s_nt = (synth.uniform(71, 8, ((N + 127) // 128) * (a.shape[0] // 128)).reshape(-1, a.shape[0] // 128) * 3
+            + 0.1).astype(np.float32)                                # [ceil(N/128), K/128]
+    sfb = np.ascontiguousarray(np.repeat(s_nt.T, 128, axis=1)[:, :N])   # [K/128, N]
+    d = oracle.k_grouped_tn(a, sfa, b, sfb, ks, None)
+    k0 = 0
+    for g, kg in enumerate(ks):
+        a_g = np.ascontiguousarray(a[k0:k0 + kg].T)                  # [M, kg]
+        b_g = np.ascontiguousarray(b[k0:k0 + kg].T)                  # [N, kg]
+        sfa_g = np.zeros((kg // 128, oracle.sf_aligned(M)), np.float32)
+        sfa_g[:, :M] = sfa[k0 // 128:(k0 + kg) // 128]
+        sfb_g = np.ascontiguousarray(s_nt[:, k0 // 128:(k0 + kg) // 128])
+        assert np.array_equal(d[g], oracle.gemm_nt(a_g, sfa_g, b_g, sfb_g, None)), g
+        k0 += kg
+
+
+def test_k_grouped_split_group_sums_and_sampled_form():
+    M, N = 16, 48
+    a, sfa, b, sfb, _, _ = _kg_problem(72, [384], M, N, with_c=False)
+    whole = oracle.k_grouped_tn(a, sfa, b, sfb, np.array([384], np.int32))
+    parts = oracle.k_grouped_tn(a, sfa, b, sfb, np.array([128, 256], np.int32))
+    mag = oracle.k_grouped_tn(a & np.uint8(0x7F), sfa, b & np.uint8(0x7F), sfb, np.array([384], np.int32))
+    assert np.all(np.abs(parts[0] + parts[1] - whole[0]) <= 2.0 ** -48 * mag[0])
+    gs = np.array([0, 1, 1, 0], np.int32)
+    ms = np.array([0, 15, 3, 7], np.int32)
+    ns = np.array([47, 0, 20, 9], np.int32)
+    at = oracle.k_grouped_tn_at(a, sfa, b, sfb, np.array([128, 256], np.int32), None, gs, ms, ns)
+    assert np.array_equal(at, parts[gs, ms, ns])
