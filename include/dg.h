@@ -240,6 +240,39 @@ int dg_fp8_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *kv_scale
                       int clean_logits, float *logits,
                       int S, int H, int D, int S_kv, void *stream);
 
+/*
+ * K-grouped FP8 GEMM, TN contiguous layout (the MoE weight-gradient form;
+ * "DeepGEMM" README summary, section "Dense and Grouped GEMM": groups along
+ * K, M and N fixed, k_grouped_fp8_gemm_tn_contiguous).  The K rows of G
+ * groups are concatenated; group g owns rows [k0_g, k0_g + ks[g]) with
+ * k0_g = ks[0] + .. + ks[g-1], and for every group (an empty one included)
+ *   D[g][m][n] = C[g][m][n] + sum_{kb in g} sfa[kb][m] * sfb[kb][n] * sum_{k in kb} A[k][m] B[k][n]
+ *   a   [K][M]        E4M3 (stored K-major in rows: A^T of the usual layout)
+ *   sfa [K/128][M]    fp32, one scale per 128 K rows and column m
+ *   b   [K][N]        E4M3
+ *   sfb [K/128][N]    fp32, one scale per 128 K rows and column n (both
+ *                     operands are activations or gradients, quantised
+ *                     1x128 along K)
+ *   ks  [G]           int32 group sizes in K rows, in DEVICE memory: each a
+ *                     multiple of 128, sum <= K.  Not checked on the host; a
+ *                     negative size counts as 0 and ranges are clamped to
+ *                     K, so a bad size gives wrong groups but no access
+ *                     outside the operands.
+ *   c   [G][M][N]     fp32 or NULL (= 0); may alias d exactly
+ *   d   [G][M][N]     fp32, written entirely.
+ * Accumulation as in dg_fp8_gemm_nt (fp32, one promotion per 128-row K
+ * block), so D meets the GEMMs' bar without their final bf16 rounding:
+ * |D - D_ref| <= 2^-20 |D_ref| + 1e-4 max|D_ref|.  Needs M and N multiples
+ * of 16, K*M and K*N below 2^31.
+ * Errors: DG_ERR_NULL (a, sfa, b, sfb, ks, d), DG_ERR_SHAPE (M, N, G < 1;
+ * K < 128 or K % 128; K*M or K*N too large), DG_ERR_ALIGN (M or N not a
+ * multiple of 16; a, sfa, b, sfb, c, d not 16-B aligned; ks not 4-B aligned).
+ */
+int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t *a, const float *sfa,
+                                        const uint8_t *b, const float *sfb,
+                                        const int32_t *ks, const float *c, float *d,
+                                        int M, int N, int K, int G, void *stream);
+
 /* Row alignment of expert segments in the contiguous layout (128).  The
  * setter accepts only 128 and returns DG_ERR_ARG otherwise. ("Utilities and
  * environment variables" section.) */

@@ -56,6 +56,9 @@ EXPORTS = {
                                   ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
     "dg_fp8_gemm_tt": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                   ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_k_grouped_fp8_gemm_tn_contiguous": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                       ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int,
+                                                       ct.c_int, ct.c_int, ct.c_void_p]),
     "dg_fp8_mqa_logits": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                      ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
                                      ct.c_void_p]),
@@ -166,6 +169,21 @@ def fp8_gemm(layout, a, sfa, b, sfb, d, c=None):
             _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
     name = "dg_fp8_gemm_" + layout
     _check(getattr(lib(), name)(*args), name)
+    return d
+
+
+def k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d, c=None):
+    """K-grouped TN contiguous GEMM (dg_k_grouped_fp8_gemm_tn_contiguous): a[K,M], b[K,N] E4M3,
+    sfa[K/128,M], sfb[K/128,N] fp32, ks[G] int32 device tensor of group sizes (multiples of 128),
+    d (and c, optional, may be d) fp32 [G,M,N]:  D[g] = C[g] + A_g^T B_g."""
+    K, M = a.shape
+    N = b.shape[1]
+    G = ks.shape[0]
+    args = (_ptr(a, _FP8, "a", (K, M)), _ptr(sfa, torch.float32, "sfa", (K // 128, M)),
+            _ptr(b, _FP8, "b", (K, N)), _ptr(sfb, torch.float32, "sfb", (K // 128, N)),
+            _ptr(ks, torch.int32, "ks", (G,)), _ptr(c, torch.float32, "c", (G, M, N)),
+            _ptr(d, torch.float32, "d", (G, M, N)), M, N, K, G, _stream(d))
+    _check(lib().dg_k_grouped_fp8_gemm_tn_contiguous(*args), "dg_k_grouped_fp8_gemm_tn_contiguous")
     return d
 
 

@@ -138,6 +138,26 @@ int dg_fp8_gemm_tt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t
     return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, false);
 }
 
+int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                                        const int32_t *ks, const float *c, float *d, int M, int N, int K, int G,
+                                        void *stream) {
+    if (!a || !sfa || !b || !sfb || !ks || !d) return DG_ERR_NULL;
+    if (M < 1 || N < 1 || G < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if ((int64_t)K * M >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31) ||
+        (int64_t)G * M * N >= ((int64_t)1 << 62))
+        return DG_ERR_SHAPE;
+    if (M % 16 != 0 || N % 16 != 0) return DG_ERR_ALIGN;
+    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+        (reinterpret_cast<uintptr_t>(ks) & 3u) || (c && !aligned16(c)))
+        return DG_ERR_ALIGN;
+    dg::GemmProblem p{a, sfa, b, sfb, nullptr, nullptr, ks, M, N, K, M, G, dg::Mode::KGrouped, 0, false};
+    p.a_mn = true;
+    p.b_mn = true;
+    p.c32 = c;
+    p.d32 = d;
+    return run_gemm(p, stream);
+}
+
 int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                    const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
     return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false);

@@ -22,7 +22,10 @@ hipError_t launch_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *k
                              const int32_t *k_start, const int32_t *k_end, int clean_logits, float *logits, int S,
                              int H, int Skv, hipStream_t stream, std::string &config);
 
-enum class Mode : int { Dense = 0, Contig = 1, Masked = 2 };
+// KGrouped: groups along K (the TN contiguous layout of MoE weight
+// gradients): A [K][M], B [K][N], `idx` = group sizes in K rows, sfa
+// [K/128][M], sfb [K/128][N], fp32 C and D [G][M][N] (c32, d32).
+enum class Mode : int { Dense = 0, Contig = 1, Masked = 2, KGrouped = 3 };
 
 // Arguments of one GEMM launch.  Per group, A has `rows_a` rows (dense: M,
 // contiguous: M_total, masked: M_cap) and its scales have leading dimension
@@ -45,6 +48,9 @@ struct GemmProblem {
     // dense only: A stored MN-major as [K][M] (TN, TT layouts), B as [K][N]
     // (NN, TN); only the pipelined family takes these
     bool a_mn = false, b_mn = false;
+    // K-grouped only: fp32 C (or NULL) and D
+    const float *c32 = nullptr;
+    float *d32 = nullptr;
 };
 
 // Skinny-M family: dense with M <= 128, and the masked layout; needs K >= 256

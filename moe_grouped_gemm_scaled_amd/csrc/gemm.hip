@@ -311,6 +311,7 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
         case Mode::Dense: return launch_tiled<128, 128, 2, 2, Mode::Dense>(p, stream, config);
         case Mode::Contig: return launch_tiled<128, 128, 2, 2, Mode::Contig>(p, stream, config);
         case Mode::Masked: return launch_tiled<128, 128, 2, 2, Mode::Masked>(p, stream, config);
+        case Mode::KGrouped: break;                    // the pipelined family only
         }
     }
     // Decode-shaped dense problems with enough 128-column tiles to occupy
@@ -336,6 +337,7 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
     case Mode::Masked:
         if (skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
         return launch_tiled<128, 128, 2, 2, Mode::Masked>(p, stream, config);
+    case Mode::KGrouped: break;                    // the pipelined family only
     }
     return hipErrorInvalidValue;
 }

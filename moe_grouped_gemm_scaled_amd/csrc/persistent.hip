@@ -731,6 +731,7 @@ hipError_t launch_persist(const GemmProblem &p, int num_cus, hipStream_t stream,
         return launch_persist_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false>(p, cus, stream, config);
     case Mode::Masked:
         return launch_persist_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false>(p, cus, stream, config);
+    case Mode::KGrouped: break;                    // the pipelined family only
     }
     return hipErrorInvalidValue;
 }

@@ -62,6 +62,9 @@ struct PipeParams {
     int splits_lo, split_hi, slots;
     // row pitch (bytes) of an operand stored MN-major: A as [K][lda], B as [K][ldb]
     int lda, ldb;
+    // K-grouped layout: fp32 C (or NULL) and D, [G][rows_a][N]
+    const float *c32;
+    float *d32;
 };
 
 // Contiguous layout with 256-row tiles: the u-th "unit" of 256 rows.  Units
@@ -146,7 +149,11 @@ pipe_kernel(PipeParams p) {
     static_assert(TM % EPI_ROWS == 0 && (TN % 8) == 0, "epilogue chunks");
     static_assert((!AMN || (BM == 128 || BM == 256)) && (!BMN || (BN == 128 || BN == 256)),
                   "MN-major tiles: K rows of 8 or 16 swizzled 16-byte columns, 1-KB DMA chunks of whole rows");
-    static_assert(!(AMN || BMN) || (MODE == Mode::Dense && !UE), "MN-major operands: dense layout, fp32 scales");
+    static_assert(!(AMN || BMN) || ((MODE == Mode::Dense || MODE == Mode::KGrouped) && !UE),
+                  "MN-major operands: dense or K-grouped layout, fp32 scales");
+    static_assert(MODE != Mode::KGrouped || (AMN && BMN && KS == 1 && !SPLIT),
+                  "K-grouped: both operands MN-major, one K block per stage, no split-K");
+    constexpr bool KG = MODE == Mode::KGrouped;
     static_assert(NW % 2 == 0 && (NW / 2) * EPI_ROWS * EPI_PITCH * 4 <= STAGE,
                   "epilogue staging: half the waves per stage");
 
@@ -172,7 +179,7 @@ pipe_kernel(PipeParams p) {
     const int nkb = K / kKBlock;
     const int nnb = (N + 127) / 128;
     const int tiles_per_group = p.tiles_m * p.tiles_n;
-    const int total = tiles_per_group * (MODE == Mode::Masked ? p.G : 1);
+    const int total = tiles_per_group * ((MODE == Mode::Masked || KG) ? p.G : 1);
 
     // ---- work unit: tile t_all (group, m-tile, n-tile) and, with split-K,
     // split s of S (the splits of a tile are adjacent workgroups; the first
@@ -195,7 +202,7 @@ pipe_kernel(PipeParams p) {
     }
     int t_lin = t_all;
     int grp = 0;
-    if (MODE == Mode::Masked) {
+    if (MODE == Mode::Masked || KG) {
         grp = t_lin / tiles_per_group;
         t_lin -= grp * tiles_per_group;
     }
@@ -215,9 +222,19 @@ pipe_kernel(PipeParams p) {
     const int n0 = tn * BN;
     // K range of this workgroup, in steps of KS blocks (nkb is a multiple of KS)
     const int nsteps_all = nkb / KS;
-    const int st0 = SPLIT ? (int)((int64_t)nsteps_all * s / S) : 0;
-    const int st1 = SPLIT ? (int)((int64_t)nsteps_all * (s + 1) / S) : nsteps_all;
-    const int nblk = st1 - st0;                    // steps
+    int st0 = SPLIT ? (int)((int64_t)nsteps_all * s / S) : 0;
+    int st1 = SPLIT ? (int)((int64_t)nsteps_all * (s + 1) / S) : nsteps_all;
+    if constexpr (KG) {
+        // the group's K rows: after the sizes of the groups before it
+        // (negative sizes count as 0; the range is clamped to [0, K])
+        int k0 = 0;
+        for (int h = 0; h < grp; ++h) k0 += max(p.idx[h], 0);
+        const int k1 = min(k0 + max(p.idx[grp], 0), K);
+        k0 = min(k0, K);
+        st0 = k0 / kKBlock;
+        st1 = st0 + max(k1 - k0, 0) / kKBlock;
+    }
+    const int nblk = st1 - st0;                    // steps (K-grouped: may be 0)
 
     const uint8_t *A = p.a;
     const float *SFA = p.sfa;
@@ -301,13 +318,17 @@ pipe_kernel(PipeParams p) {
     // (the scales of K blocks kb .. kb+3; all of these waves write the same
     // bytes).  Lanes past the tile fetch harmless in-range or zero-filled data
     // into unused slots.
+    // K-grouped: B scales are per column (sfb[kb][n]); lane l of a B-scale
+    // wave fetches sfb[kb][n0 + 4l .. +3] (clamped to the last 4 columns).
     const bool wsa = wave < KS;
     const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
-        wsa ? (void *)SFA : (void *)SFB, (short)0, wsa ? nkb * ld * 4 : nnb * nkb * 4, 0x00020000);
+        wsa ? (void *)SFA : (void *)SFB, (short)0, wsa ? nkb * ld * 4 : (KG ? nkb * N * 4 : nnb * nkb * 4),
+        0x00020000);
     const int sa_row = m0 + 4 * lane;
-    const int v_s = wsa ? ((sa_row < ld ? sa_row : 0) + wave * ld) * 4 : min(n0 / 128 + lane, nnb - 1) * nkb * 4;
+    const int v_s = wsa ? ((sa_row < ld ? sa_row : 0) + wave * ld) * 4
+                        : (KG ? min(n0 + 4 * lane, N - 4) * 4 : min(n0 / 128 + lane, nnb - 1) * nkb * 4);
     const int lds_s = wsa ? OFF_SA + wave * 1024 : OFF_SB;
-    const int s_stride = wsa ? ld * 4 : 4;
+    const int s_stride = wsa ? ld * 4 : (KG ? N * 4 : 4);
 
     // DMA of step st (K blocks KS*st .. +KS-1) into stage stg
     auto dma = [&](uint8_t *stg, int st) __attribute__((always_inline)) {
@@ -374,6 +395,19 @@ pipe_kernel(PipeParams p) {
     auto compute_block = [&](const uint8_t *stg_step, auto kkc) __attribute__((always_inline)) {
         constexpr int kk = decltype(kkc)::value;
         const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
+        // K-grouped: the B scales of the lane's 4 columns of each subtile
+        v4f sbv[KG ? SN : 1];
+        if constexpr (KG) {
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                sbv[j] = *reinterpret_cast<const v4f *>(stg_step + OFF_SB + 4 * (wn * TN + 16 * j + 4 * g4));
+            });
+        }
+        // acc + p * (sa * sb): one B scale per wave and K block, or (K-grouped) one per column
+        auto prom = [&](const v4f &a, const v4f &pv, float sa_v, auto jc) __attribute__((always_inline)) {
+            if constexpr (KG) return promote(a, pv, sbv[decltype(jc)::value] * sa_v);
+            else return promote(a, pv, sa_v * sb);
+        };
         const uint8_t *stg = stg_step + kk * BLK_A;        // A block kk; B block kk is at stg_b
         const uint8_t *stg_b = stg_step + kk * BLK_B;
         const uint8_t *stg_s = stg_step + kk * 1024;       // A scales of block kk
@@ -415,10 +449,9 @@ pipe_kernel(PipeParams p) {
                     pp[j] = mfma_16x16x128_e4m3(bf[j], af_cur, v4f{0.f, 0.f, 0.f, 0.f});
                 });
                 if constexpr (i > 0) {
-                    const float sv = sa_prv * sb;
                     static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                         constexpr int j = decltype(jc)::value;
-                        acc[i - 1][j] = promote(acc[i - 1][j], pp_prv[j], sv);
+                        acc[i - 1][j] = prom(acc[i - 1][j], pp_prv[j], sa_prv, jc);
                     });
                 }
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
@@ -430,10 +463,9 @@ pipe_kernel(PipeParams p) {
                     sa_cur = sa_nxt;
                 }
             });
-            const float sv = sa_prv * sb;
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
-                acc[SM - 1][j] = promote(acc[SM - 1][j], pp_prv[j], sv);
+                acc[SM - 1][j] = prom(acc[SM - 1][j], pp_prv[j], sa_prv, jc);
             });
         } else {
             // promote each subtile right after its MFMAs (the other wave on the
@@ -446,10 +478,9 @@ pipe_kernel(PipeParams p) {
                     constexpr int j = decltype(jc)::value;
                     pp[j] = mfma_16x16x128_e4m3(bf[j], af_cur, v4f{0.f, 0.f, 0.f, 0.f});
                 });
-                const float sv = sa_cur * sb;
                 static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                     constexpr int j = decltype(jc)::value;
-                    acc[i][j] = promote(acc[i][j], pp[j], sv);
+                    acc[i][j] = prom(acc[i][j], pp[j], sa_cur, jc);
                 });
                 if constexpr (i + 1 < SM) {
                     af_cur = af_nxt;
@@ -511,19 +542,48 @@ pipe_kernel(PipeParams p) {
     // others; indices past the end re-fetch the last step, which is then never
     // multiplied.
     constexpr int kWaitPipe = wait_vmcnt((NST - 2) * PER_BLOCK);
+    if (!KG || nblk > 0) {                         // uniform; only an empty K group has no step
 #pragma clang loop unroll(disable)   // no peeled first round: one copy of every DMA keeps the wait counts exact
-    for (int b = -(NST - 1); b < nblk; b += NST) {
-        nested_steps<0, NST>(b, nblk, [&](auto sc) __attribute__((always_inline)) {
-            constexpr int u = decltype(sc)::value;
-            const int j = b + u;
-            __builtin_amdgcn_s_waitcnt(kWaitPipe);
-            lds_barrier();
-            dma(stage_of(sc), st0 + min(j + NST - 1, nblk - 1));
-            if (j >= 0) compute(stage_of(std::integral_constant<int, (u + 1) % NST>{}));
-        });
+        for (int b = -(NST - 1); b < nblk; b += NST) {
+            nested_steps<0, NST>(b, nblk, [&](auto sc) __attribute__((always_inline)) {
+                constexpr int u = decltype(sc)::value;
+                const int j = b + u;
+                __builtin_amdgcn_s_waitcnt(kWaitPipe);
+                lds_barrier();
+                dma(stage_of(sc), st0 + min(j + NST - 1, nblk - 1));
+                if (j >= 0) compute(stage_of(std::integral_constant<int, (u + 1) % NST>{}));
+            });
+        }
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     lds_barrier();
+
+    // ---- K-grouped epilogue: fp32 D = C + acc straight from the registers
+    // (lane l holds row 16i + l%16 and columns 16j + 4(l/16) .. +3 of its
+    // wave's tile: one 16-byte access each; M and N are multiples of 16)
+    if constexpr (KG) {
+        float *D32 = p.d32 + (int64_t)grp * rows_a * N;
+        const float *C32 = p.c32 ? p.c32 + (int64_t)grp * rows_a * N : nullptr;
+        static_for<SM>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            const int row = m0 + wm * TM + 16 * i + l16;
+            v4f cv[SN];
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                const int col = n0 + wn * TN + 16 * j + 4 * g4;
+                cv[j] = v4f{0.f, 0.f, 0.f, 0.f};
+                if (C32 && row < rows_a && col < N)
+                    cv[j] = *reinterpret_cast<const v4f *>(C32 + (int64_t)row * N + col);
+            });
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                const int col = n0 + wn * TN + 16 * j + 4 * g4;
+                if (row < rows_a && col < N)
+                    *reinterpret_cast<v4f *>(D32 + (int64_t)row * N + col) = acc[i][j] + cv[j];
+            });
+        });
+        return;
+    }
 
     // ---- split-K: every split publishes its partial; the last to arrive sums
     // all of them in split order and finishes the tile
@@ -653,6 +713,8 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
     k.rows_a = p.rows_a; k.N = p.N; k.K = p.K; k.ld_sfa = p.ld_sfa; k.G = p.G;
     k.lda = p.rows_a;
     k.ldb = p.N;
+    k.c32 = p.c32;
+    k.d32 = p.d32;
     k.tiles_m = (p.rows_a + BM - 1) / BM;
     if (MODE == Mode::Contig && BM == 256) {
         // units: at most one per 256 rows plus one per expert segment
@@ -667,7 +729,7 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
     k.split_hi = 0;
     k.slots = 1;
     if ((p.K / kKBlock) % KS != 0) return hipErrorInvalidValue;
-    const int64_t groups = MODE == Mode::Masked ? p.G : 1;
+    const int64_t groups = (MODE == Mode::Masked || MODE == Mode::KGrouped) ? p.G : 1;
     const int64_t tiles = (int64_t)k.tiles_m * k.tiles_n * groups;
     const int nsteps = p.K / kKBlock / KS;
     int64_t grid = tiles;
@@ -756,6 +818,7 @@ static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t 
         return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false, UE>(p, 0, stream, config);
     case Mode::Masked:
         return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false, UE>(p, 0, stream, config);
+    case Mode::KGrouped: break;                    // launched by launch_pipe
     }
     return hipErrorInvalidValue;
 }
@@ -775,6 +838,15 @@ static hipError_t launch_pipe_layout(const GemmProblem &p, int num_cus, hipStrea
 
 hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     if (!pipe_eligible(p)) return hipErrorInvalidValue;
+    if (p.mode == Mode::KGrouped) {
+        // K-grouped (TN, fp32 D): 256x256 tiles when both M and N fill them
+        if (!p.a_mn || !p.b_mn || p.ue8m0 || !p.d32) return hipErrorInvalidValue;
+        if (p.rows_a >= 256 && p.N >= 256)
+            return launch_pipe_t<256, 256, 2, 4, 2, 1, false, Mode::KGrouped, false, false, true, true>(p, 0, stream,
+                                                                                                   config);
+        return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::KGrouped, false, false, true, true>(p, 0, stream,
+                                                                                               config);
+    }
     if (p.a_mn || p.b_mn) {
         if (p.mode != Mode::Dense || p.ue8m0) return hipErrorInvalidValue;
         if (p.a_mn && p.b_mn) return launch_pipe_layout<true, true>(p, num_cus, stream, config);

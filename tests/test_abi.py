@@ -163,3 +163,19 @@ def test_layout_argument_errors(lib):
     assert lib.dg_fp8_gemm_tn(P, P, 64, P, P, NULL, P, 64, 72, 128, S) == -3      # N % 16
     assert lib.dg_fp8_gemm_tt(P, P, 72, P, P, NULL, P, 72, 64, 128, S) == -3      # M % 16
     assert lib.dg_fp8_gemm_nn(P, P, 64, P, P, NULL, P, 64, 72, 128, S) == -3      # N % 16
+
+
+def test_k_grouped_argument_errors(lib):
+    f = lib.dg_k_grouped_fp8_gemm_tn_contiguous
+    # a, sfa, b, sfb, ks, c, d, M, N, K, G, stream
+    assert f(NULL, P, P, P, P, NULL, P, 64, 64, 128, 2, S) == -1
+    assert f(P, P, P, P, NULL, NULL, P, 64, 64, 128, 2, S) == -1
+    assert f(P, P, P, P, P, NULL, NULL, 64, 64, 128, 2, S) == -1
+    assert f(P, P, P, P, P, NULL, P, 64, 64, 100, 2, S) == -2        # K % 128
+    assert f(P, P, P, P, P, NULL, P, 64, 64, 128, 0, S) == -2        # G < 1
+    assert f(P, P, P, P, P, NULL, P, 0, 64, 128, 2, S) == -2
+    assert f(P, P, P, P, P, NULL, P, 1 << 20, 64, 4096, 2, S) == -2  # K * M reaches 2^31
+    assert f(P, P, P, P, P, NULL, P, 72, 64, 128, 2, S) == -3        # M % 16
+    assert f(P, P, P, P, P, NULL, P, 64, 40, 128, 2, S) == -3        # N % 16
+    assert f(MIS, P, P, P, P, NULL, P, 64, 64, 128, 2, S) == -3
+    assert f(P, P, P, P, ct.c_void_p(0x10002), NULL, P, 64, 64, 128, 2, S) == -3
