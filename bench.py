@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload decode|prefill|contiguous|masked|small|prefill_ue8m0|contiguous_ue8m0|mqa|
-                                prefill_nn|prefill_tn|prefill_tt]
+                                prefill_nn|prefill_tn|prefill_tt|kgrouped]
 
 A step is one pass of the hot path over one batch of synthetic input: for
 every GEMM of the workload, quantise the fp32 activations (1x128 scales) and
@@ -203,6 +203,36 @@ def masked_jobs():
 # timing
 # ---------------------------------------------------------------------------
 
+def kgrouped_jobs():
+    """One K-grouped TN contiguous GEMM (MoE weight gradient): operands
+    quantised 1x128 along K by the library's quantiser and laid out [K, M],
+    [K, N] beforehand; fp32 D, no C."""
+    cfg = synth.KGROUPED
+    M, N = cfg["M"], cfg["N"]
+    ksn = synth.kgrouped_sizes(cfg)
+    K = int(ksn.sum())
+    G = ksn.size
+    xa = torch.from_numpy(synth.normal_f32(cfg["seed"], synth.STREAM_A, (M, K))).cuda()
+    qa, sa = dg.quantize_e4m3_1x128(xa, ld_sf=M)
+    del xa
+    xb = torch.from_numpy(synth.normal_f32(cfg["seed"], synth.STREAM_B, (N, K))).cuda()
+    qb, sb = dg.quantize_e4m3_1x128(xb, ld_sf=N)
+    del xb
+    a, b = qa.t().contiguous(), qb.t().contiguous()
+    sfa, sfb = sa.contiguous(), sb.contiguous()
+    ks = torch.from_numpy(ksn).cuda()
+    d = torch.empty((G, M, N), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def launch(ci, with_quant):
+        dg.k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d)
+
+    flops = 2.0 * M * N * K
+    nbytes = K * M + K * N + 4 * (K // 128) * (M + N) + 4 * G + 4 * G * M * N
+    meta = {"G": G, "M": M, "N": N, "K_total": K, "ks": ksn.tolist()}
+    return [Job(cfg["name"], launch, 1, flops, nbytes, 0)], meta
+
+
 def mqa_jobs():
     """One FP8 MQA logits call (the v3.2 indexer's scoring) over a causal
     prefill chunk; inputs are already E4M3 (as the indexer holds them)."""
@@ -376,7 +406,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "contiguous", "masked", "small", "prefill_ue8m0", "contiguous_ue8m0",
-                             "mqa", "prefill_nn", "prefill_tn", "prefill_tt"])
+                             "mqa", "prefill_nn", "prefill_tn", "prefill_tt", "kgrouped"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB each (reference for HBM byte counters)")
@@ -414,6 +444,9 @@ def main():
         bound = "mfma"
     elif args.workload in ("prefill_nn", "prefill_tn", "prefill_tt"):
         jobs = dense_jobs(synth.PREFILL, layout=args.workload[-2:])
+        bound = "mfma"
+    elif args.workload == "kgrouped":
+        jobs, meta = kgrouped_jobs()
         bound = "mfma"
     elif args.workload == "mqa":
         jobs, meta = mqa_jobs()
@@ -499,6 +532,9 @@ def main():
                       "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
         "prefill_tt": "prefill-shaped dense FP8 GEMM in the TT layout (A stored [K,M], B [N,K]), M=4096 x (N,K) in "
                       "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
+        "kgrouped": "K-grouped TN contiguous FP8 GEMM (MoE weight gradient), 8 groups of the contiguous workload's "
+                    "token counts padded to 128 (K_total 17408), M=7168, N=2048, 1x128 scales on both operands, "
+                    "fp32 D, no C",
         "mqa": "FP8 MQA logits (non-paged, clean_logits): 4096 query tokens x 64 heads x 128 against 8192 keys, "
                "causal ranges, fp32 logits [4096, 8192]",
     }[args.workload]
@@ -521,7 +557,7 @@ def main():
         "config": {"workload": workload_desc,
                    "step": ("one fp8_mqa_logits call, inputs resident" if args.workload == "mqa" else
                             "one GEMM per shape, operands quantised and laid out beforehand"
-                            if args.workload[-3:] in ("_nn", "_tn", "_tt") else
+                            if args.workload[-3:] in ("_nn", "_tn", "_tt") or args.workload == "kgrouped" else
                             "activation quantiser + GEMM per shape; weights pre-quantised"),
                    "graph_replay": True, **({"layout": meta} if meta else {})},
         "roofline": roof,

@@ -192,8 +192,8 @@ def packed_ranges(lengths):
 # K-grouped TN contiguous (MoE weight gradient): the expert down-projection's
 # weight gradient dW[g] = dY_g^T X_g, with M = 7168 (hidden), N = 2048 (expert
 # intermediate) and the 8 experts' token counts of the contiguous workload,
-# each padded to 128 rows, as the K groups.
-KGROUPED = dict(name="kgrouped_g8_m7168_n2048", G=8, M=7168, N=2048, with_c=True, seed=SEED_BASE + 6)
+# each padded to 128 rows, as the K groups; no C (a fresh gradient).
+KGROUPED = dict(name="kgrouped_g8_m7168_n2048", G=8, M=7168, N=2048, with_c=False, seed=SEED_BASE + 6)
 
 
 def kgrouped_sizes(cfg=KGROUPED) -> np.ndarray:
