@@ -11,9 +11,10 @@ before timing, as in inference.  Default workload: the decode-shaped dense
 GEMMs, M in {64, 128} x (N, K) in {(2112, 7168), (24576, 1536), (7168, 16384)},
 C = 0, bf16 D.
 
-Timing: each distinct step is captured once in a HIP graph (so host launch
-cost does not stall the GPU) and the timed region replays exactly K steps,
-bracketed by device synchronisation.  Weight copies rotate so that every B
+Timing: the W warm-up steps and the K timed steps are each captured as one
+HIP graph of consecutive steps (so host launch cost does not stall the GPU);
+the timed region is one replay of the K-step graph, bracketed by device
+synchronisation.  Weight copies rotate so that every B
 is re-read only after more than 512 MB of other traffic (the 256 MB
 Infinity Cache cannot serve it).  Per-kernel durations for the roofline are
 measured separately with HIP events around graph replays of one GEMM launch
@@ -462,10 +463,18 @@ def main():
         bound = "hbm"
     log(f"workload {args.workload}: {[j.name for j in jobs]}, copies {[j.copies for j in jobs]}")
 
-    # step graphs: step s uses weight copy s of every job (period = max copies)
-    period = max(j.copies for j in jobs)
-    n_graphs = min(period, max(2, args.steps + args.warmup))
-    graphs = [capture(lambda s=s: [j.launch(s, True) for j in jobs]) for s in range(n_graphs)]
+    # two graphs: the W warm-up steps and the K timed steps, each captured as
+    # one graph of consecutive steps (step s uses weight copy s of every job),
+    # so that a replay boundary never sits between two timed steps
+    def steps_fn(first, count):
+        def fn():
+            for s in range(first, first + count):
+                for j in jobs:
+                    j.launch(s, True)
+        return fn
+
+    warm_graph = capture(steps_fn(0, args.warmup)) if args.warmup > 0 else None
+    timed_graph = capture(steps_fn(args.warmup, args.steps))
     configs = []
     with torch.cuda.stream(_CAPTURE_STREAM):       # the stream the graphs were captured on
         for j in jobs:
@@ -473,12 +482,11 @@ def main():
             configs.append(dg.last_config())
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        graphs[i % n_graphs].replay()
+    if warm_graph is not None:
+        warm_graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % n_graphs].replay()
+    timed_graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
