@@ -206,6 +206,26 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t *a, const float *sfa,
                                           const int32_t *masked_m,
                                           int G, int M_cap, int N, int K,
                                           int expected_m, void *stream);
+/* The same for the other layouts and the K-grouped form (declared below),
+ * with the same power-of-two requirement on every scale.  In the K-grouped
+ * form each lane hands the matrix instruction the exponent of its own B
+ * column, so the per-column scales cost no promotion either. */
+int dg_fp8_gemm_nn_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa,
+                         const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d,
+                         int M, int N, int K, void *stream);
+int dg_fp8_gemm_tn_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa,
+                         const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d,
+                         int M, int N, int K, void *stream);
+int dg_fp8_gemm_tt_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa,
+                         const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d,
+                         int M, int N, int K, void *stream);
+int dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(const uint8_t *a, const float *sfa,
+                                              const uint8_t *b, const float *sfb,
+                                              const int32_t *ks, const float *c, float *d,
+                                              int M, int N, int K, int G, void *stream);
 
 /*
  * FP8 MQA logits, non-paged (the DeepSeek v3.2 indexer's scoring kernel;

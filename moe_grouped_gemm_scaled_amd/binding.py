@@ -59,6 +59,15 @@ EXPORTS = {
     "dg_k_grouped_fp8_gemm_tn_contiguous": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                                        ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int,
                                                        ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_fp8_gemm_nn_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                        ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_fp8_gemm_tn_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                        ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_fp8_gemm_tt_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                        ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                             ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int,
+                                                             ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
     "dg_fp8_mqa_logits": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                      ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
                                      ct.c_void_p]),
@@ -152,7 +161,7 @@ def fp8_gemm_nt(a, sfa, b, sfb, d, c=None, ue8m0=False):
     return d
 
 
-def fp8_gemm(layout, a, sfa, b, sfb, d, c=None):
+def fp8_gemm(layout, a, sfa, b, sfb, d, c=None, ue8m0=False):
     """D = C + A @ B in one of the layouts "nt", "nn", "tn", "tt" (dg_fp8_gemm_<layout>).
     The first letter is A's storage: "n" a[M,K], "t" a[K,M]; the second B's: "t" b[N,K], "n" b[K,N].
     Scales as for fp8_gemm_nt: sfa[K/128, ld_sfa], sfb[ceil(N/128), K/128]; d/c[M,N] bf16."""
@@ -167,12 +176,12 @@ def fp8_gemm(layout, a, sfa, b, sfb, d, c=None):
     args = (_ptr(a, _FP8, "a", a_shape), _ptr(sfa, torch.float32, "sfa"), int(sfa.shape[1]),
             _ptr(b, _FP8, "b", b_shape), _ptr(sfb, torch.float32, "sfb", (ceil_div(N, 128), K // 128)),
             _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
-    name = "dg_fp8_gemm_" + layout
+    name = _name("dg_fp8_gemm_" + layout, ue8m0)
     _check(getattr(lib(), name)(*args), name)
     return d
 
 
-def k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d, c=None):
+def k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d, c=None, ue8m0=False):
     """K-grouped TN contiguous GEMM (dg_k_grouped_fp8_gemm_tn_contiguous): a[K,M], b[K,N] E4M3,
     sfa[K/128,M], sfb[K/128,N] fp32, ks[G] int32 device tensor of group sizes (multiples of 128),
     d (and c, optional, may be d) fp32 [G,M,N]:  D[g] = C[g] + A_g^T B_g."""
@@ -183,7 +192,8 @@ def k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d, c=None):
             _ptr(b, _FP8, "b", (K, N)), _ptr(sfb, torch.float32, "sfb", (K // 128, N)),
             _ptr(ks, torch.int32, "ks", (G,)), _ptr(c, torch.float32, "c", (G, M, N)),
             _ptr(d, torch.float32, "d", (G, M, N)), M, N, K, G, _stream(d))
-    _check(lib().dg_k_grouped_fp8_gemm_tn_contiguous(*args), "dg_k_grouped_fp8_gemm_tn_contiguous")
+    name = _name("dg_k_grouped_fp8_gemm_tn_contiguous", ue8m0)
+    _check(getattr(lib(), name)(*args), name)
     return d
 
 

@@ -108,7 +108,7 @@ static int masked_impl(const uint8_t *a, const float *sfa, const uint8_t *b, con
 // multiple of 16) and 32-bit buffer offsets (K * M, K * N below 2^31).
 static int gemm_layout_impl(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                             const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream, bool a_mn,
-                            bool b_mn) {
+                            bool b_mn, bool ue8m0) {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_NULL;
     if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if ((int64_t)K * M >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31)) return DG_ERR_SHAPE;
@@ -117,7 +117,7 @@ static int gemm_layout_impl(const uint8_t *a, const float *sfa, int ld_sfa, cons
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
         (c && !aligned16(c)))
         return DG_ERR_ALIGN;
-    dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, false};
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, ue8m0};
     p.a_mn = a_mn;
     p.b_mn = b_mn;
     return run_gemm(p, stream);
@@ -125,22 +125,37 @@ static int gemm_layout_impl(const uint8_t *a, const float *sfa, int ld_sfa, cons
 
 int dg_fp8_gemm_nn(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                    const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
-    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false, true);
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false, true, false);
+}
+
+int dg_fp8_gemm_nn_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false, true, true);
 }
 
 int dg_fp8_gemm_tn(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                    const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
-    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, true);
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, true, false);
+}
+
+int dg_fp8_gemm_tn_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, true, true);
 }
 
 int dg_fp8_gemm_tt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                    const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
-    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, false);
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, false, false);
 }
 
-int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
-                                        const int32_t *ks, const float *c, float *d, int M, int N, int K, int G,
-                                        void *stream) {
+int dg_fp8_gemm_tt_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                         const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_layout_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true, false, true);
+}
+
+static int k_grouped_impl(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                          const int32_t *ks, const float *c, float *d, int M, int N, int K, int G, void *stream,
+                          bool ue8m0) {
     if (!a || !sfa || !b || !sfb || !ks || !d) return DG_ERR_NULL;
     if (M < 1 || N < 1 || G < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if ((int64_t)K * M >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31) ||
@@ -150,12 +165,24 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t *a, const float *sfa, cons
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
         (reinterpret_cast<uintptr_t>(ks) & 3u) || (c && !aligned16(c)))
         return DG_ERR_ALIGN;
-    dg::GemmProblem p{a, sfa, b, sfb, nullptr, nullptr, ks, M, N, K, M, G, dg::Mode::KGrouped, 0, false};
+    dg::GemmProblem p{a, sfa, b, sfb, nullptr, nullptr, ks, M, N, K, M, G, dg::Mode::KGrouped, 0, ue8m0};
     p.a_mn = true;
     p.b_mn = true;
     p.c32 = c;
     p.d32 = d;
     return run_gemm(p, stream);
+}
+
+int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
+                                        const int32_t *ks, const float *c, float *d, int M, int N, int K, int G,
+                                        void *stream) {
+    return k_grouped_impl(a, sfa, b, sfb, ks, c, d, M, N, K, G, stream, false);
+}
+
+int dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(const uint8_t *a, const float *sfa, const uint8_t *b,
+                                              const float *sfb, const int32_t *ks, const float *c, float *d, int M,
+                                              int N, int K, int G, void *stream) {
+    return k_grouped_impl(a, sfa, b, sfb, ks, c, d, M, N, K, G, stream, true);
 }
 
 int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,

@@ -149,8 +149,8 @@ pipe_kernel(PipeParams p) {
     static_assert(TM % EPI_ROWS == 0 && (TN % 8) == 0, "epilogue chunks");
     static_assert((!AMN || (BM == 128 || BM == 256)) && (!BMN || (BN == 128 || BN == 256)),
                   "MN-major tiles: K rows of 8 or 16 swizzled 16-byte columns, 1-KB DMA chunks of whole rows");
-    static_assert(!(AMN || BMN) || ((MODE == Mode::Dense || MODE == Mode::KGrouped) && !UE),
-                  "MN-major operands: dense or K-grouped layout, fp32 scales");
+    static_assert(!(AMN || BMN) || MODE == Mode::Dense || MODE == Mode::KGrouped,
+                  "MN-major operands: dense or K-grouped layout");
     static_assert(MODE != Mode::KGrouped || (AMN && BMN && KS == 1 && !SPLIT),
                   "K-grouped: both operands MN-major, one K block per stage, no split-K");
     constexpr bool KG = MODE == Mode::KGrouped;
@@ -499,10 +499,20 @@ pipe_kernel(PipeParams p) {
     // biased fp32 exponent field of each scale: one for the wave's B block,
     // one per lane for its A row) and accumulates straight into acc, so no
     // fresh partial per K block and no promotion on the VALU.
+    // K-grouped: the first operand's exponent is per lane too, from the
+    // scale of the B column (row of the B fragment) the lane holds.
     auto compute_block_ue = [&](const uint8_t *stg_step, auto kkc) __attribute__((always_inline)) {
         constexpr int kk = decltype(kkc)::value;
         const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
         const int eb = (int)(__float_as_uint(sb) >> 23);
+        int ebj[KG ? SN : 1];
+        if constexpr (KG) {
+            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                const float sbj = *reinterpret_cast<const float *>(stg_step + OFF_SB + 4 * (wn * TN + 16 * j + l16));
+                ebj[j] = (int)(__float_as_uint(sbj) >> 23);
+            });
+        }
         const uint8_t *stg = stg_step + kk * BLK_A;
         const uint8_t *stg_b = stg_step + kk * BLK_B;
         const uint8_t *stg_s = stg_step + kk * 1024;
@@ -519,14 +529,19 @@ pipe_kernel(PipeParams p) {
         });
         static_for<SM>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
-            const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a0[0] + i * 16 * kKBlock);
-            const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
-            const v8i af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            v8i af;
+            if constexpr (AMN) {
+                af = read_frag_tr<BM>(stg + off_amn[i]);
+            } else {
+                const v4i lo = *reinterpret_cast<const v4i *>(stg + off_a0[0] + i * 16 * kKBlock);
+                const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
+                af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
             const float sa = *reinterpret_cast<const float *>(stg_s + off_sa0 + i * 64);
             const int ea = (int)(__float_as_uint(sa) >> 23);
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
-                acc[i][j] = mfma_16x16x128_e4m3_scaled(bf[j], af, acc[i][j], eb, ea);
+                acc[i][j] = mfma_16x16x128_e4m3_scaled(bf[j], af, acc[i][j], KG ? ebj[KG ? j : 0] : eb, ea);
             });
         });
     };
@@ -831,32 +846,41 @@ static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t 
 // Dense GEMMs with an operand stored MN-major (the NN, TN and TT layouts):
 // the prefill tiles of the NT path (256x256 for long K or a whole number of
 // waves of tiles, 128x128 otherwise), without split-K.
-template <bool AMN, bool BMN>
+template <bool AMN, bool BMN, bool UE>
 static hipError_t launch_pipe_layout(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     const int cus = num_cus > 0 ? num_cus : 256;
     const int nkb = p.K / kKBlock;
     const int64_t t256 = (int64_t)((p.rows_a + 255) / 256) * ((p.N + 255) / 256);
     if (p.rows_a >= 256 && (nkb > 16 || t256 % cus == 0))
-        return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, false, AMN, BMN>(p, 0, stream, config);
-    return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, false, AMN, BMN>(p, 0, stream, config);
+        return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, UE, AMN, BMN>(p, 0, stream, config);
+    return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, UE, AMN, BMN>(p, 0, stream, config);
+}
+
+template <bool UE>
+static hipError_t launch_pipe_kgrouped(const GemmProblem &p, hipStream_t stream, std::string &config) {
+    // 256x256 tiles when both M and N fill them (without DEEP: with it the
+    // per-column scales spill); 128x128 otherwise
+    if (p.rows_a >= 256 && p.N >= 256)
+        return launch_pipe_t<256, 256, 2, 4, 2, 1, false, Mode::KGrouped, false, UE, true, true>(p, 0, stream, config);
+    return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::KGrouped, false, UE, true, true>(p, 0, stream, config);
 }
 
 hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     if (!pipe_eligible(p)) return hipErrorInvalidValue;
     if (p.mode == Mode::KGrouped) {
-        // K-grouped (TN, fp32 D): 256x256 tiles when both M and N fill them
-        if (!p.a_mn || !p.b_mn || p.ue8m0 || !p.d32) return hipErrorInvalidValue;
-        if (p.rows_a >= 256 && p.N >= 256)
-            return launch_pipe_t<256, 256, 2, 4, 2, 1, false, Mode::KGrouped, false, false, true, true>(p, 0, stream,
-                                                                                                   config);
-        return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::KGrouped, false, false, true, true>(p, 0, stream,
-                                                                                               config);
+        if (!p.a_mn || !p.b_mn || !p.d32) return hipErrorInvalidValue;
+        return p.ue8m0 ? launch_pipe_kgrouped<true>(p, stream, config) : launch_pipe_kgrouped<false>(p, stream, config);
     }
     if (p.a_mn || p.b_mn) {
-        if (p.mode != Mode::Dense || p.ue8m0) return hipErrorInvalidValue;
-        if (p.a_mn && p.b_mn) return launch_pipe_layout<true, true>(p, num_cus, stream, config);
-        if (p.a_mn) return launch_pipe_layout<true, false>(p, num_cus, stream, config);
-        return launch_pipe_layout<false, true>(p, num_cus, stream, config);
+        if (p.mode != Mode::Dense) return hipErrorInvalidValue;
+        if (p.ue8m0) {
+            if (p.a_mn && p.b_mn) return launch_pipe_layout<true, true, true>(p, num_cus, stream, config);
+            if (p.a_mn) return launch_pipe_layout<true, false, true>(p, num_cus, stream, config);
+            return launch_pipe_layout<false, true, true>(p, num_cus, stream, config);
+        }
+        if (p.a_mn && p.b_mn) return launch_pipe_layout<true, true, false>(p, num_cus, stream, config);
+        if (p.a_mn) return launch_pipe_layout<true, false, false>(p, num_cus, stream, config);
+        return launch_pipe_layout<false, true, false>(p, num_cus, stream, config);
     }
     return p.ue8m0 ? launch_pipe_ue<true>(p, num_cus, stream, config) : launch_pipe_ue<false>(p, num_cus, stream, config);
 }

@@ -179,3 +179,14 @@ def test_k_grouped_argument_errors(lib):
     assert f(P, P, P, P, P, NULL, P, 64, 40, 128, 2, S) == -3        # N % 16
     assert f(MIS, P, P, P, P, NULL, P, 64, 64, 128, 2, S) == -3
     assert f(P, P, P, P, ct.c_void_p(0x10002), NULL, P, 64, 64, 128, 2, S) == -3
+
+
+def test_ue8m0_layout_and_k_grouped_argument_errors(lib):
+    for name in ("dg_fp8_gemm_nn_ue8m0", "dg_fp8_gemm_tn_ue8m0", "dg_fp8_gemm_tt_ue8m0"):
+        f = getattr(lib, name)
+        assert f(NULL, P, 64, P, P, NULL, P, 64, 64, 128, S) == -1, name
+        assert f(P, P, 64, P, P, NULL, P, 64, 64, 100, S) == -2, name
+    assert lib.dg_fp8_gemm_tn_ue8m0(P, P, 72, P, P, NULL, P, 72, 64, 128, S) == -3
+    f = lib.dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0
+    assert f(P, P, P, P, NULL, NULL, P, 64, 64, 128, 2, S) == -1
+    assert f(P, P, P, P, P, NULL, P, 64, 40, 128, 2, S) == -3

@@ -168,3 +168,57 @@ def test_prefill_ue8m0_full_size_sampled(cfg):
     ref = oracle.gemm_nt_at(p["a"], p["sfa"], p["b"], p["sfb"], p["c"], mm.reshape(-1), nn.reshape(-1))
     check_close(got[mm, nn].reshape(-1), ref, cfg["name"] + " ue8m0")
     assert not np.any((got & 0x7F80) == 0x7F80), "non-finite output"
+
+
+# ---- the other layouts and the K-grouped form with power-of-two scales
+
+def _stored(layout, a, b):
+    a_st = np.ascontiguousarray(a.T) if layout[0] == "t" else a
+    b_st = np.ascontiguousarray(b.T) if layout[1] == "n" else b
+    return a_st, b_st
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("M,N,K,with_c", [(256, 384, 512, True), (304, 528, 2304, False)])
+def test_layout_ue8m0(layout, M, N, K, with_c):
+    announce(f"layout {layout} ue8m0 M={M} N={N} K={K}")
+    p = dense_problem(M, N, K, seed=M + N + K + 5, with_c=with_c, ue8m0=True)
+    a_st, b_st = _stored(layout, p["a"], p["b"])
+    out = Guarded((M, N))
+    c = dev_bf16(p["c"]) if p["c"] is not None else None
+    dg.fp8_gemm(layout, dev(a_st), dev(p["sfa"]), dev(b_st), dev(p["sfb"]), out.t, c=c, ue8m0=True)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    cfg = dg.last_config()
+    assert "scales=ue8m0" in cfg and f"layout={layout}" in cfg, cfg
+    ref = oracle.gemm_layout(layout, a_st, p["sfa"], b_st, p["sfb"], p["c"])
+    check_close(out.bits(), ref, f"{layout} ue8m0 {M}x{N}x{K} ({cfg})")
+
+
+@pytest.mark.parametrize("ks,M,N", [([256, 0, 128, 384], 128, 144), ([512, 128, 640], 272, 400)])
+def test_k_grouped_ue8m0(ks, M, N):
+    """Power-of-two scales on both operands: the matrix instruction applies
+    the A row's and the B column's exponents per lane."""
+    announce(f"k-grouped ue8m0 ks={ks} M={M} N={N}")
+    K = int(np.sum(ks))
+    seed = 95 + M + N
+    qa, sa = oracle.quantize_1x128(synth.normal_f32(seed, synth.STREAM_A, (M, K)), ld_sf=M, ue8m0=True)
+    qb, sb = oracle.quantize_1x128(_wide_range(seed, (N, K)), ld_sf=N, ue8m0=True)
+    a, b = np.ascontiguousarray(qa.T), np.ascontiguousarray(qb.T)
+    sfa, sfb = sa[:, :M].copy(), sb[:, :N].copy()
+    ksa = np.asarray(ks, np.int32)
+    c = synth.normal_f32(seed, synth.STREAM_C, (len(ks), M, N))
+    d = torch.full((len(ks), M, N), float("nan"), dtype=torch.float32, device="cuda")
+    dg.k_grouped_fp8_gemm_tn_contiguous(dev(a), dev(sfa), dev(b), dev(sfb), dev(ksa), d, c=dev(c), ue8m0=True)
+    torch.cuda.synchronize()
+    assert "scales=ue8m0" in dg.last_config(), dg.last_config()
+    got = d.cpu().numpy().astype(np.float64)
+    ref = oracle.k_grouped_tn(a, sfa, b, sfb, ksa, c)
+    for g in range(len(ks)):
+        if ks[g] == 0:
+            assert np.array_equal(got[g], c[g].astype(np.float64))
+            continue
+        scale = float(np.max(np.abs(ref[g])))
+        tol = 2.0 ** -20 * np.abs(ref[g]) + 1e-4 * scale
+        bad = ~(np.abs(got[g] - ref[g]) <= tol)
+        assert not np.any(bad), (g, np.argwhere(bad)[:5], got[g][bad][:5], ref[g][bad][:5])
