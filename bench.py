@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload decode|prefill|contiguous|masked|small|prefill_ue8m0|contiguous_ue8m0|mqa|
-                                prefill_nn|prefill_tn|prefill_tt|kgrouped]
+                                prefill_nn|prefill_tn|prefill_tt|kgrouped|kgrouped_ue8m0]
 
 A step is one pass of the hot path over one batch of synthetic input: for
 every GEMM of the workload, quantise the fp32 activations (1x128 scales) and
@@ -204,7 +204,7 @@ def masked_jobs():
 # timing
 # ---------------------------------------------------------------------------
 
-def kgrouped_jobs():
+def kgrouped_jobs(ue8m0=False):
     """One K-grouped TN contiguous GEMM (MoE weight gradient): operands
     quantised 1x128 along K by the library's quantiser and laid out [K, M],
     [K, N] beforehand; fp32 D, no C."""
@@ -214,10 +214,10 @@ def kgrouped_jobs():
     K = int(ksn.sum())
     G = ksn.size
     xa = torch.from_numpy(synth.normal_f32(cfg["seed"], synth.STREAM_A, (M, K))).cuda()
-    qa, sa = dg.quantize_e4m3_1x128(xa, ld_sf=M)
+    qa, sa = dg.quantize_e4m3_1x128(xa, ld_sf=M, ue8m0=ue8m0)
     del xa
     xb = torch.from_numpy(synth.normal_f32(cfg["seed"], synth.STREAM_B, (N, K))).cuda()
-    qb, sb = dg.quantize_e4m3_1x128(xb, ld_sf=N)
+    qb, sb = dg.quantize_e4m3_1x128(xb, ld_sf=N, ue8m0=ue8m0)
     del xb
     a, b = qa.t().contiguous(), qb.t().contiguous()
     sfa, sfb = sa.contiguous(), sb.contiguous()
@@ -226,7 +226,7 @@ def kgrouped_jobs():
     torch.cuda.synchronize()
 
     def launch(ci, with_quant):
-        dg.k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d)
+        dg.k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d, ue8m0=ue8m0)
 
     flops = 2.0 * M * N * K
     nbytes = K * M + K * N + 4 * (K // 128) * (M + N) + 4 * G + 4 * G * M * N
@@ -407,7 +407,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "contiguous", "masked", "small", "prefill_ue8m0", "contiguous_ue8m0",
-                             "mqa", "prefill_nn", "prefill_tn", "prefill_tt", "kgrouped"])
+                             "mqa", "prefill_nn", "prefill_tn", "prefill_tt", "kgrouped", "kgrouped_ue8m0"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB each (reference for HBM byte counters)")
@@ -446,8 +446,8 @@ def main():
     elif args.workload in ("prefill_nn", "prefill_tn", "prefill_tt"):
         jobs = dense_jobs(synth.PREFILL, layout=args.workload[-2:])
         bound = "mfma"
-    elif args.workload == "kgrouped":
-        jobs, meta = kgrouped_jobs()
+    elif args.workload in ("kgrouped", "kgrouped_ue8m0"):
+        jobs, meta = kgrouped_jobs(ue8m0=args.workload.endswith("_ue8m0"))
         bound = "mfma"
     elif args.workload == "mqa":
         jobs, meta = mqa_jobs()
@@ -543,6 +543,9 @@ def main():
         "kgrouped": "K-grouped TN contiguous FP8 GEMM (MoE weight gradient), 8 groups of the contiguous workload's "
                     "token counts padded to 128 (K_total 17408), M=7168, N=2048, 1x128 scales on both operands, "
                     "fp32 D, no C",
+        "kgrouped_ue8m0": "K-grouped TN contiguous FP8 GEMM (MoE weight gradient), 8 groups of the contiguous "
+                          "workload's token counts padded to 128 (K_total 17408), M=7168, N=2048, power-of-two "
+                          "(UE8M0) 1x128 scales on both operands, fp32 D, no C",
         "mqa": "FP8 MQA logits (non-paged, clean_logits): 4096 query tokens x 64 heads x 128 against 8192 keys, "
                "causal ranges, fp32 logits [4096, 8192]",
     }[args.workload]
@@ -565,7 +568,7 @@ def main():
         "config": {"workload": workload_desc,
                    "step": ("one fp8_mqa_logits call, inputs resident" if args.workload == "mqa" else
                             "one GEMM per shape, operands quantised and laid out beforehand"
-                            if args.workload[-3:] in ("_nn", "_tn", "_tt") or args.workload == "kgrouped" else
+                            if args.workload[-3:] in ("_nn", "_tn", "_tt") or args.workload.startswith("kgrouped") else
                             "activation quantiser + GEMM per shape; weights pre-quantised"),
                    "graph_replay": True, **({"layout": meta} if meta else {})},
         "roofline": roof,
