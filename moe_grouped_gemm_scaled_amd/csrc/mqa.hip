@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void mqa_kernel(MqaParams p) {
                 v4f v;
                 if (j >= lo && j + 4 <= hi) v = *reinterpret_cast<const v4f *>(rv);
                 else v = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                *reinterpret_cast<v4f *>(orow + j) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(orow + j));   // streaming: not read again
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {

@@ -490,7 +490,8 @@ persist_kernel(PersistParams p) {
                 }
                 if (ok) {
                     if (vec) {
-                        *reinterpret_cast<v4i *>(D + o) = v4i{w4[0], w4[1], w4[2], w4[3]};
+                        // streaming store (D is not read again)
+                        __builtin_nontemporal_store(v4i{w4[0], w4[1], w4[2], w4[3]}, reinterpret_cast<v4i *>(D + o));
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
