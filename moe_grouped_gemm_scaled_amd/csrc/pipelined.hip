@@ -820,15 +820,12 @@ static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t 
             }
             return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true, UE>(p, cus, stream, config);
         }
-        // prefill shapes.  256x256 tiles (8 waves of 128x64, two stages) read
-        // the fewest bytes from LDS and from L2 per MFMA.  With short K (few
-        // blocks per tile) and a last wave of tiles that leaves CUs idle,
-        // 128x128 tiles with two workgroups per CU do better: one
-        // workgroup's epilogue and pipeline fill overlap the other's MFMAs
-        // (measured on MI355X for M = 4096 and (N, K) in {(4096, 7168),
-        // (7168, 2048), (24576, 1536)}).
-        const int64_t t256 = (int64_t)((p.rows_a + 255) / 256) * ((p.N + 255) / 256);
-        if (p.rows_a >= 256 && (nkb > 16 || t256 % cus == 0))
+        // prefill shapes: 256x256 tiles (8 waves of 128x64, two stages) read
+        // the fewest bytes from LDS and from L2 per MFMA.  With streaming D
+        // stores they beat 128x128, 128x256 and 256x128 tiles on every
+        // measured shape (MI355X, M = 4096, (N, K) in {(4096, 7168): 107 us,
+        // (7168, 2048): 77 against 92 us for 128x128, (24576, 1536): 208 us}).
+        if (p.rows_a >= 256)
             return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, UE>(p, 0, stream, config);
         return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, UE>(p, 0, stream, config);
     }
@@ -847,14 +844,12 @@ static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t 
 }
 
 // Dense GEMMs with an operand stored MN-major (the NN, TN and TT layouts):
-// the prefill tiles of the NT path (256x256 for long K or a whole number of
-// waves of tiles, 128x128 otherwise), without split-K.
+// the prefill tiles of the NT path (256x256 from 256 rows, 128x128 below),
+// without split-K.
 template <bool AMN, bool BMN, bool UE>
 static hipError_t launch_pipe_layout(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
-    const int cus = num_cus > 0 ? num_cus : 256;
-    const int nkb = p.K / kKBlock;
-    const int64_t t256 = (int64_t)((p.rows_a + 255) / 256) * ((p.N + 255) / 256);
-    if (p.rows_a >= 256 && (nkb > 16 || t256 % cus == 0))
+    (void)num_cus;
+    if (p.rows_a >= 256)
         return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, UE, AMN, BMN>(p, 0, stream, config);
     return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, UE, AMN, BMN>(p, 0, stream, config);
 }
