@@ -1,5 +1,8 @@
 /*
- * dg.h -- C ABI of the MI355X (gfx950) FP8 block-scaled NT GEMM library.
+ * dg.h -- C ABI of the MI355X (gfx950) FP8 block-scaled GEMM library: the
+ * NT GEMM and its M-grouped MoE forms, the E4M3 quantisers, the NN/TN/TT
+ * layouts, the K-grouped weight-gradient GEMM, power-of-two (UE8M0) scale
+ * variants, and the FP8 MQA logits.
  *
  * Operation (the "DeepGEMM" README summary on GeekNews, ja.news.hada.io topic
  * 19459, section "GEMM interface and layout constraints"): D = C + A . B^T in
@@ -13,7 +16,8 @@
  *
  *   D[m,n] = C[m,n] + sum_kb sfa[kb][m] * sfb[n/128][kb] * sum_{k in kb} A[m,k] B[n,k]
  *
- * Conventions for every entry point:
+ * Conventions for every entry point (a declaration below states any
+ * exception, e.g. the fp32 outputs of the K-grouped GEMM and the MQA logits):
  *  - Types: E4M3 values are uint8_t bit patterns (OCP E4M3FN: bias 7, no
  *    infinities, max 448); bf16 values are uint16_t bit patterns; scales fp32.
  *  - All tensors are dense, row-major (last index fastest), in device memory
@@ -26,7 +30,8 @@
  *  - D is bf16, rounded to nearest even from the fp32 accumulator.  C is bf16
  *    of the same shape as D, or NULL for C = 0; C may alias D exactly.
  *  - K must be a positive multiple of 128.  M and N may be any positive size
- *    (partial row and column tiles are handled).
+ *    (partial row and column tiles are handled), except where an operand is
+ *    stored MN-major (multiples of 16).
  *  - Dense calls with a small M use split-K: they keep an internal fp32
  *    workspace per device and stream (allocated on first use, grown when a
  *    larger problem arrives, freed at process exit).  Calls on one stream
