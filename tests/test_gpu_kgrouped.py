@@ -135,3 +135,21 @@ def test_k_grouped_full_size_sampled():
         gs = np.full(mm.size, g, np.int32)
         ref = oracle.k_grouped_tn_at(a, sfa, b, sfb, ksa, c, gs, mm.reshape(-1), nn.reshape(-1))
         check(got[g][mm, nn].reshape(-1), ref, f"{cfg['name']} group {g} ({dg.last_config()})")
+
+
+def test_k_grouped_many_groups_with_empties():
+    """40 groups of 0 to 512 rows (a third empty): the per-tile scan over the
+    group sizes and the group-major tile numbering."""
+    sizes = synth.randint(86, 3, 40, 0, 4) * 128
+    sizes[::3] = 0
+    ks = sizes.astype(np.int32)
+    M, N = 128, 160
+    announce(f"k-grouped 40 groups, K={int(ks.sum())}")
+    a, sfa, b, sfb, ksa, c = problem(86, ks, M, N, True)
+    got = run(a, sfa, b, sfb, ksa, c)
+    ref = oracle.k_grouped_tn(a, sfa, b, sfb, ksa, c)
+    for g in range(len(ks)):
+        if ks[g] == 0:
+            assert np.array_equal(got[g], c[g]), g
+        else:
+            check(got[g], ref[g], f"group {g}")

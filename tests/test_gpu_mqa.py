@@ -211,3 +211,17 @@ def test_mqa_logits_full_size_sampled():
     inside = cols < ke[:, None]
     assert np.all(np.isfinite(got[inside]))
     assert np.all(np.isneginf(got[~inside]))
+
+
+def test_mqa_logits_long_key_axis():
+    """Few queries against 70 000 keys (137 chunks), ranges that start and end
+    deep inside the key axis, and one range over all of it."""
+    S, H, S_kv = 3, 64, 70000
+    announce(f"mqa long key axis S={S} S_kv={S_kv}")
+    q, kv, kv_scale, weights = synth.mqa_tensors(65, S, H, S_kv)
+    ks = np.array([0, 33333, 69990], np.int32)
+    ke = np.array([S_kv, 50001, 70100], np.int32)
+    for clean in (True, False):
+        got = run(q, kv, kv_scale, weights, ks, ke, clean)
+        ref = oracle.mqa_logits(q, kv, kv_scale, weights, ks, ke, clean)
+        check(got, ref, magnitude(q, kv, kv_scale, weights, ks, ke), clean, f"long keys clean={clean}")
