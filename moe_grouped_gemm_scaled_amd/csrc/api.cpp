@@ -158,9 +158,7 @@ static int k_grouped_impl(const uint8_t *a, const float *sfa, const uint8_t *b, 
                           bool ue8m0) {
     if (!a || !sfa || !b || !sfb || !ks || !d) return DG_ERR_NULL;
     if (M < 1 || N < 1 || G < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
-    if ((int64_t)K * M >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31) ||
-        (int64_t)G * M * N >= ((int64_t)1 << 62))
-        return DG_ERR_SHAPE;
+    if ((int64_t)K * M >= ((int64_t)1 << 31) || (int64_t)K * N >= ((int64_t)1 << 31)) return DG_ERR_SHAPE;
     if (M % 16 != 0 || N % 16 != 0) return DG_ERR_ALIGN;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
         (reinterpret_cast<uintptr_t>(ks) & 3u) || (c && !aligned16(c)))
@@ -273,7 +271,7 @@ int dg_fp8_mqa_logits(const uint8_t *q, const uint8_t *kv, const float *kv_scale
                       int D, int S_kv, void *stream) {
     if (!q || !kv || !kv_scale || !weights || !k_start || !k_end || !logits) return DG_ERR_NULL;
     if (S < 1 || S_kv < 1 || D != 128 || H < 16 || H > 64 || H % 16 != 0) return DG_ERR_SHAPE;
-    if ((long long)S_kv * D >= (1LL << 31) || (long long)S * H * D >= (1LL << 62)) return DG_ERR_SHAPE;
+    if ((long long)S_kv * D >= (1LL << 31)) return DG_ERR_SHAPE;   // 32-bit buffer offsets into kv
     if (!aligned16(q) || !aligned16(kv) || !aligned16(weights) || (reinterpret_cast<uintptr_t>(kv_scale) & 3u) ||
         (reinterpret_cast<uintptr_t>(k_start) & 3u) || (reinterpret_cast<uintptr_t>(k_end) & 3u) ||
         (reinterpret_cast<uintptr_t>(logits) & 3u))
