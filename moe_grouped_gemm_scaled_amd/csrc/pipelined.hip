@@ -1,7 +1,10 @@
-// pipelined.hip -- FP8 block-scaled NT GEMM for gfx950 with a multi-stage
-// LDS pipeline filled by DMA: one kernel template for decode shapes (few
-// rows, long K, optional split-K), prefill shapes and the M-grouped
-// contiguous and masked layouts.
+// pipelined.hip -- FP8 block-scaled GEMM for gfx950 with a multi-stage LDS
+// pipeline filled by DMA: one kernel template for decode shapes (few rows,
+// long K, optional split-K), prefill shapes, the M-grouped contiguous and
+// masked layouts, operands stored MN-major (the NN, TN and TT layouts, read
+// through transposing LDS loads), the K-grouped TN layout of MoE weight
+// gradients (fp32 D, per-column B scales) and power-of-two scales applied by
+// the scaled MFMA.
 //
 // Arithmetic (per 128-wide K block: one v_mfma_f32_16x16x128_f8f6f4 partial
 // per 16x16 subtile, promoted into the fp32 accumulator with
@@ -31,9 +34,11 @@
 //    writeback or invalidate is needed;
 //  - the epilogue loads all of C under a wave's tile at once, then stages the
 //    fp32 tile through LDS in 32-row chunks so that D is written as 16-byte
-//    row segments.
+//    row segments, with streaming (nontemporal) stores; the K-grouped
+//    epilogue writes fp32 D straight from the accumulators.
 // Without split-K, workgroups are numbered so that consecutive tiles of one
-// group run on the same XCD (shared L2) in a grouped raster.
+// group run on the same XCD (shared L2) in a grouped raster; K-grouped tiles,
+// whose lengths differ by group, keep dispatch order instead.
 #include <stdio.h>
 #include <stdlib.h>
 
