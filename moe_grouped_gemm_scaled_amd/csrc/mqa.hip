@@ -27,8 +27,8 @@
 //    tile (two xor-shuffle rounds that also spread the results so that
 //    every lane ends with NQ finished logits);
 //  - finished logits go to an LDS row buffer; after the chunk each wave
-//    writes its rows once, masked, as 16-byte stores (a vmcnt-free main
-//    loop: no global store competes with the pipeline's load counts).
+//    writes its rows once, masked, as 16-byte streaming stores (a main loop
+//    without global stores: none competes with the pipeline's load counts).
 // Workgroups are numbered so that the chunks of one query block run on one
 // XCD (the queries' fragments are re-read from its L2), while consecutive
 // query blocks, whose ranges differ in length, spread over all XCDs.
