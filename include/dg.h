@@ -116,9 +116,11 @@ int dg_fp8_gemm_tt(const uint8_t *a, const float *sfa, int ld_sfa,
  *   b   [G][N][K] E4M3;     sfb [G][ceil(N/128)][K/128] fp32
  *   c   [M_total][N] bf16 or NULL;  d [M_total][N] bf16
  *   m_indices [M_total] int32 in device memory: the expert of each row, or -1
- *             on padding rows.  Rows with -1 are neither computed nor written.
+ *             on padding rows.  Rows with -1 are neither computed nor written;
+ *             a 128-row block whose first id lies outside [0, G) is treated
+ *             as padding too (so a bad id never reads outside b and sfb).
  * Precondition (not checked on the device): each aligned 128-row block holds
- * rows of at most one expert, valid rows first; ids are in [-1, G).
+ * rows of at most one expert, valid rows first.
  * Errors: DG_ERR_NULL, DG_ERR_SHAPE (M_total % 128, N, K, G < 1), DG_ERR_ALIGN.
  */
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t *a, const float *sfa,

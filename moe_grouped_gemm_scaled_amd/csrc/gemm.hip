@@ -99,7 +99,7 @@ gemm_tiled_kernel(GemmParams p) {
         D += (int64_t)grp * rows_a * N;
     } else if (MODE == Mode::Contig) {
         const int e = p.idx[m0];
-        if (e < 0) return;                // tile of padding rows: uniform exit
+        if (e < 0 || e >= p.G) return;    // padding (or an invalid id): uniform exit
         B += (int64_t)e * N * K;
         SFB += (int64_t)e * nnb * nkb;
     }

@@ -157,7 +157,7 @@ persist_kernel(PersistParams p) {
                         nvalid = mm - tm * BM < BM ? mm - tm * BM : BM;
                     } else {
                         const int e = p.idx[cidx * BM];
-                        ok = e >= 0;
+                        ok = e >= 0 && e < p.G;            // padding or an invalid id: no tile
                         entry = (e << 16) | cidx;
                     }
                 }

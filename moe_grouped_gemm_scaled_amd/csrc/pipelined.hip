@@ -270,7 +270,7 @@ pipe_kernel(PipeParams p) {
     int expert = 0;                                // contiguous: the tile's expert; its rows are the ones stored
     if (MODE == Mode::Contig) {
         expert = p.idx[m0];
-        if (expert < 0) return;                    // tile of padding rows: uniform exit
+        if (expert < 0 || expert >= p.G) return;   // padding (or an invalid id): uniform exit
         B += (int64_t)expert * N * K;
         SFB += (int64_t)expert * nnb * nkb;
     }

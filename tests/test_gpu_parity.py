@@ -338,3 +338,33 @@ def test_split_k_on_concurrent_streams():
         for k, ((p, *_), out, ref) in enumerate(zip(probs, outs, refs)):
             assert out.guards_intact()
             check_close(out.bits(), ref, f"stream {k} rep {rep}")
+
+
+@pytest.mark.parametrize("family", ["auto", "pipe", "persist", "tiled"])
+def test_contiguous_invalid_expert_ids_are_padding(family):
+    """A 128-row block whose id lies outside [0, G) (too large, or negative
+    other than -1) is padding: never computed, never written, and b is never
+    read past its last expert."""
+    counts = [130, 128, 70]
+    N, K = 256, 384
+    announce(f"contiguous invalid ids, family {family}")
+    p = contiguous_problem(counts, N, K, seed=23, with_c=False)
+    G = len(counts)
+    idx = p["m_indices"].copy()
+    idx[256:384] = G + 3                  # expert 1's block: an id past the last expert
+    idx[384:454] = -5                     # expert 2's rows: a negative id other than -1
+    clean = np.where((idx >= 0) & (idx < G), idx, -1).astype(np.int32)
+    out = Guarded((p["M_total"], N))
+    dg.set_kernel_family(family)
+    try:
+        dg.m_grouped_fp8_gemm_nt_contiguous(dev(p["a"]), dev(p["sfa"]), dev(p["b"]), dev(p["sfb"]), out.t,
+                                            dev(idx))
+        torch.cuda.synchronize()
+    finally:
+        dg.set_kernel_family("auto")
+    assert out.guards_intact()
+    got = out.bits()
+    ref = oracle.m_grouped_contiguous(p["a"], p["sfa"], p["b"], p["sfb"], None, clean)
+    valid = clean >= 0
+    check_close(got[valid], ref[valid], f"contiguous valid rows ({family})")
+    assert np.all(got[~valid] == SENTINEL)
