@@ -386,7 +386,8 @@ bool get_splitk_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters
             w.ws = nullptr;
             return false;
         }
-        if (hipMemset(w.counters, 0, nc * sizeof(int)) != hipSuccess) return false;
+        // on the stream itself, so that the zeroing precedes the stream's next kernels
+        if (hipMemsetAsync(w.counters, 0, nc * sizeof(int), stream) != hipSuccess) return false;
         w.ws_bytes = nb;
         w.n_counters = nc;
     }
