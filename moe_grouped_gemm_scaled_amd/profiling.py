@@ -12,6 +12,17 @@
         N bytes (`bench.py --copy-calibration`), plus the hash of the kernel
         sources the counters were taken on.
 
+    python -m moe_grouped_gemm_scaled_amd.profiling mfma --bench-json B.json \\
+            --util U.db --ops O.db
+        JSON: per GEMM launch of each benchmark job, the matrix-core and LDS
+        counters of one `rocprofv3 --pmc MfmaUtil LdsUtil LDSBankConflict
+        VALUBusy` run and one `--pmc SQ_INSTS_VALU_MFMA_MOPS_F8
+        SQ_INSTS_VALU_MFMA_MOPS_F6F4 GRBM_GUI_ACTIVE` run of the benchmark:
+        MFMA-busy, LDS-busy, bank-conflict and VALU-busy percentages, the FP8
+        matrix operations counted (MOPS x 512) against the job's algorithmic
+        flops, and the GPU clock implied by the active-cycle count over the
+        dispatch duration.
+
 The databases are the `*_results.db` files rocprofv3 writes (SQLite); only
 the standard library is used to read them.
 """
@@ -73,6 +84,65 @@ def counter_values(db, counter):
     for name, wg, v in rows:
         out.setdefault((name, int(wg)), []).append(float(v))
     return out
+
+
+def per_dispatch(db, counter):
+    """{(kernel display name, workgroups): [(counter value, rows, duration ns) per dispatch]}: the rows
+    of one dispatch (one per hardware instance, for counters reported per shader engine or XCD)
+    are summed."""
+    con = sqlite3.connect(db)
+    t = _tables(con)
+    kd, ks, pe, ip = (t("rocpd_kernel_dispatch_"), t("rocpd_info_kernel_symbol_"), t("rocpd_pmc_event_"),
+                      t("rocpd_info_pmc_"))
+    rows = con.execute(f"select s.display_name, d.grid_size_x / d.workgroup_size_x, d.end - d.start, "
+                       f"sum(p.value), count(*) "
+                       f"from {pe} p join {kd} d on p.event_id = d.event_id join {ks} s on d.kernel_id = s.id "
+                       f"join {ip} i on p.pmc_id = i.id where i.name = ? group by p.event_id", (counter,)).fetchall()
+    con.close()
+    out = {}
+    for name, wg, dur, v, n in rows:
+        out.setdefault((name, int(wg)), []).append((float(v), int(n), float(dur)))
+    return out
+
+
+def _job_values(table, frag, grid):
+    hits = [v for (n, g), v in table.items() if frag in n and g == grid]
+    return hits[0] if len(hits) == 1 else None
+
+
+def mfma(bench_json, util_db, ops_db):
+    with open(bench_json) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    util = {c: per_dispatch(util_db, c) for c in ("MfmaUtil", "LdsUtil", "LDSBankConflict", "VALUBusy")}
+    ops = {c: per_dispatch(ops_db, c) for c in ("SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4",
+                                                 "GRBM_GUI_ACTIVE")}
+    jobs = {}
+    for job in bench["per_gemm"]:
+        frag, grid = _kernel_fragment(job["config"])
+        rec = {}
+        for c, table in util.items():
+            v = _job_values(table, frag, grid)
+            rec[c + "_pct"] = None if v is None else statistics.mean(x for x, _n, _d in v)
+        f8 = _job_values(ops["SQ_INSTS_VALU_MFMA_MOPS_F8"], frag, grid)
+        f64 = _job_values(ops["SQ_INSTS_VALU_MFMA_MOPS_F6F4"], frag, grid)
+        gui = _job_values(ops["GRBM_GUI_ACTIVE"], frag, grid)
+        flops = job["gemm_TFLOPs"] * 1e12 * job["gemm_us"] * 1e-6
+        rec["algorithmic_flop_per_launch"] = flops
+        if f8 is not None and f64 is not None:
+            counted = 512.0 * (statistics.mean(x for x, _n, _d in f8) + statistics.mean(x for x, _n, _d in f64))
+            rec["mfma_ops_counted_per_launch"] = counted
+            rec["counted_over_algorithmic"] = counted / flops if flops else None
+        if gui is not None:
+            # GRBM_GUI_ACTIVE is reported per XCD (8 rows per dispatch when not aggregated); the clock is
+            # the cycles of one XCD over the dispatch duration
+            cyc = statistics.mean(x / max(n, 1) for x, n, _d in gui)
+            dur = statistics.mean(d for _x, _n, d in gui)
+            rec["gui_active_cycles_per_xcd"] = cyc
+            rec["rows_per_dispatch"] = gui[0][1]
+            rec["dispatch_us_under_counters"] = dur / 1e3
+            rec["clock_ghz"] = cyc / dur if dur > 0 else None
+        jobs[job["name"]] = rec
+    return {"workload": bench["config"]["workload"], "source_hash": kernel_source_hash(), "jobs": jobs}
 
 
 def stats_table(db, min_calls=1):
@@ -159,9 +229,15 @@ def main(argv=None):
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--bench-json", required=True)
+    m.add_argument("--util", required=True)
+    m.add_argument("--ops", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.db, a.min_calls))
+    elif a.cmd == "mfma":
+        print(json.dumps(mfma(a.bench_json, a.util, a.ops), indent=1))
     else:
         print(json.dumps(traffic(a.bench_json, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes),
                          indent=1))
