@@ -121,6 +121,18 @@ __device__ __forceinline__ int contig_unit_block(const int32_t *idx, int nblocks
     return -1;
 }
 
+// Swizzle of the 16-byte columns of K row r of an MN-major LDS tile with CPR
+// columns per row.  (r & 7) spreads the eight rows that one 16-lane group of
+// a transposing read touches over eight column positions.  In 256-byte rows
+// (CPR = 16) those eight positions cover only half of the banks, so
+// ((r >> 4) & 1) selects the half: the groups g and g+1 of a read (rows
+// 16g + j) then fall on different banks.  The swizzle is the same for rows
+// 16g + j, +8, +64 and +72 (j < 8), the four rows one lane reads per fragment.
+template <int CPR>
+__device__ __forceinline__ int mn_swizzle(int r) {
+    return CPR == 16 ? ((r & 7) | (((r >> 4) & 1) << 3)) : (r & 7);
+}
+
 // AMN / BMN: A (B) is stored MN-major, as [K][M] ([K][N]); its LDS tiles
 // then hold K rows of BM (BN) bytes and fragments are read with transposing
 // LDS loads (read_frag_tr).
@@ -298,7 +310,7 @@ pipe_kernel(PipeParams p) {
     int va[DA], vb[DB];
     // MN-major operand: chunk c holds K rows RPC*(c / KS) .. +RPC-1 of K
     // block c % KS (RPC = 1024 / BM rows of BM bytes); lane l lands at row
-    // +l/CPR, 16-byte column l%CPR and fetches column (l%CPR) ^ (row & 7).
+    // +l/CPR, 16-byte column l%CPR and fetches column (l%CPR) ^ mn_swizzle<CPR>(row).
     // Columns past M (N) clamp to the row's last 16 bytes (M and N are
     // multiples of 16 here); their products are never stored.
     static_for<DA>([&](auto ic) __attribute__((always_inline)) {
@@ -306,7 +318,7 @@ pipe_kernel(PipeParams p) {
         if constexpr (AMN) {
             constexpr int CPR = BM / 16, RPC = 1024 / BM;
             const int krow = RPC * (wr + RG_STEP * i) + lane / CPR;
-            va[i] = (wk * kKBlock + krow) * p.lda + min(m0 + 16 * ((lane % CPR) ^ (krow & 7)), p.lda - 16);
+            va[i] = (wk * kKBlock + krow) * p.lda + min(m0 + 16 * ((lane % CPR) ^ mn_swizzle<CPR>(krow)), p.lda - 16);
         } else {
             va[i] = min(m0 + 8 * (wr + RG_STEP * i) + (lane >> 3), rows_a - 1) * K + wk * kKBlock + dchunk;
         }
@@ -316,7 +328,7 @@ pipe_kernel(PipeParams p) {
         if constexpr (BMN) {
             constexpr int CPR = BN / 16, RPC = 1024 / BN;
             const int krow = RPC * (wr + RG_STEP * i) + lane / CPR;
-            vb[i] = (wk * kKBlock + krow) * p.ldb + min(n0 + 16 * ((lane % CPR) ^ (krow & 7)), p.ldb - 16);
+            vb[i] = (wk * kKBlock + krow) * p.ldb + min(n0 + 16 * ((lane % CPR) ^ mn_swizzle<CPR>(krow)), p.ldb - 16);
         } else {
             vb[i] = min(n0 + 8 * (wr + RG_STEP * i) + (lane >> 3), N - 1) * K + wk * kKBlock + dchunk;
         }
@@ -376,21 +388,22 @@ pipe_kernel(PipeParams p) {
     const int off_sb = OFF_SB + 16 * wave_nb;
     // MN-major fragments: lane l of group g = l/16 addresses K row
     // 16g + (l%16)/2 and columns +8*(l & 1) of the 16-column subtile; the
-    // swizzle (row & 7) = (l%16)/2 is fixed per lane, so each subtile gets its
-    // own base offset
+    // swizzle of those rows (and of rows +8, +64, +72) is fixed per lane, so
+    // each subtile gets its own base offset
     int off_amn[AMN ? SM : 1], off_bmn[BMN ? SN : 1];
     if constexpr (AMN) {
         static_for<SM>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
             const int c = (wm * TM) / 16 + i;
-            off_amn[i] = opaque_offset((16 * g4 + (l16 >> 1)) * BM + ((c ^ ((l16 >> 1) & 7)) << 4) + 8 * (l16 & 1));
+            off_amn[i] = opaque_offset((16 * g4 + (l16 >> 1)) * BM + ((c ^ mn_swizzle<BM / 16>(16 * g4 + (l16 >> 1))) << 4) +
+                                       8 * (l16 & 1));
         });
     }
     if constexpr (BMN) {
         static_for<SN>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
             const int c = (wn * TN) / 16 + j;
-            off_bmn[j] = opaque_offset(OFF_B + (16 * g4 + (l16 >> 1)) * BN + ((c ^ ((l16 >> 1) & 7)) << 4) +
+            off_bmn[j] = opaque_offset(OFF_B + (16 * g4 + (l16 >> 1)) * BN + ((c ^ mn_swizzle<BN / 16>(16 * g4 + (l16 >> 1))) << 4) +
                                        8 * (l16 & 1));
         });
     }
