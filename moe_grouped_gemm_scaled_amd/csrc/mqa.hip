@@ -40,6 +40,12 @@
 
 namespace dg {
 
+// ReLU as a signed integer max on the bit pattern: every value with the sign
+// bit set (negatives, -0) becomes +0 and every other value passes unchanged,
+// which is exact for all finite and infinite inputs.  One VALU instruction,
+// where fmaxf(x, 0) first canonicalises x (IEEE NaN handling) with a second.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 namespace {
 
 constexpr int kMqaD = 128;        // head dim: one MFMA K
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void mqa_kernel(MqaParams p) {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) s = fmaf(wq[q][t][r], fmaxf(pr[t][r], 0.f), s);
+                        for (int r = 0; r < 4; ++r) s = fmaf(wq[q][t][r], relu_bits(pr[t][r]), s);
                     }
                     acc[q * NKT + kt] = s;
                 }
