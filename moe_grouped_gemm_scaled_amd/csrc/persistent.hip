@@ -486,7 +486,7 @@ persist_kernel(PersistParams p) {
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t u = (uint32_t)cwv[e];
                     const float c0 = bf16_to_f32((uint16_t)(u & 0xffff)), c1 = bf16_to_f32((uint16_t)(u >> 16));
-                    w4[e] = (int)(f32_to_bf16_rne(v8[2 * e] + c0) | ((uint32_t)f32_to_bf16_rne(v8[2 * e + 1] + c1) << 16));
+                    w4[e] = (int)pack_bf16x2_rne(v8[2 * e] + c0, v8[2 * e + 1] + c1);
                 }
                 if (ok) {
                     if (vec) {

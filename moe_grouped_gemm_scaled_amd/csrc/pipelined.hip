@@ -714,8 +714,7 @@ pipe_kernel(PipeParams p) {
                     for (int e = 0; e < 4; ++e) {
                         const uint32_t u = (uint32_t)cwv[e];
                         const float c0 = bf16_to_f32((uint16_t)(u & 0xffff)), c1 = bf16_to_f32((uint16_t)(u >> 16));
-                        w4[e] = (int)(f32_to_bf16_rne(v8[2 * e] + c0) |
-                                      ((uint32_t)f32_to_bf16_rne(v8[2 * e + 1] + c1) << 16));
+                        w4[e] = (int)pack_bf16x2_rne(v8[2 * e] + c0, v8[2 * e + 1] + c1);
                     }
                     // streaming store: D is not read again here, and keeping it
                     // out of L2 shortens the epilogue's write burst (measured:
