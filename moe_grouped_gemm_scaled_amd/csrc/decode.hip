@@ -54,6 +54,12 @@ struct SkinnyParams {
     int tiles_m, tiles_n, splits;
 };
 
+// 128-wide scale blocks that a tile of BN columns can touch.  Tiles start at
+// multiples of BN, so a width that is neither a multiple nor a divisor of 128
+// (96) can start inside a block and reach into the next.  Shared by the
+// kernel's LDS layout and the launcher's LDS size.
+constexpr int skinny_scale_blocks(int BN) { return BN % 128 == 0 ? BN / 128 : (128 % BN == 0 ? 1 : BN / 128 + 2); }
+
 template <int MT, int NTW, int WGM, int WGN, int KS, int PD, Mode MODE>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 skinny_kernel(SkinnyParams p) {
@@ -66,7 +72,7 @@ skinny_kernel(SkinnyParams p) {
     constexpr int RPL = NT / CR;                  // rows covered by one load of all threads
     constexpr int LA = (ROWS + RPL - 1) / RPL;    // A chunks per thread per step
     constexpr int LB = (BN + RPL - 1) / RPL;      // B chunks per thread per step
-    constexpr int NBW = BN >= 128 ? BN / 128 : 1; // 128-wide scale blocks under the workgroup's columns
+    constexpr int NBW = skinny_scale_blocks(BN);  // 128-wide scale blocks under the workgroup's columns
     constexpr int SUB_A = ROWS * kKBlock;         // one K block of A in LDS
     constexpr int SUB_B = BN * kKBlock;
     constexpr int OFF_B = KS * SUB_A;
@@ -77,7 +83,8 @@ skinny_kernel(SkinnyParams p) {
     constexpr int LS = (NSCALE + NT - 1) / NT;    // scale values per thread per step
     static_assert(MT % WGM == 0 && NTW % WGN == 0, "wave grid");
     static_assert(NT % CR == 0, "loads split evenly");
-    static_assert(BN % 128 == 0 || 128 % BN == 0, "columns vs scale blocks");
+    // a wave's columns start at a multiple of their width, which divides 128:
+    // they never straddle a scale block
     static_assert(16 * NTWW <= 128 && 128 % (16 * NTWW) == 0, "a wave's columns share one scale block");
     static_assert(PD % 2 == 0, "LDS stages alternate per step");
 
@@ -183,7 +190,8 @@ skinny_kernel(SkinnyParams p) {
             gs_off[i] = OFF_SB + 4 * (q - ROWS * KS);
         }
     });
-    const int wave_nb = (wn * NTWW * 16) / 128 < NBW ? (wn * NTWW * 16) / 128 : 0;   // scale block of this wave
+    // scale block of this wave, counted from the block of column n0
+    const int wave_nb = ((n0 & 127) + wn * NTWW * 16) / 128 < NBW ? ((n0 & 127) + wn * NTWW * 16) / 128 : 0;
 
     // ---- register ring (zeroed: the first PD steps of the loop only fill it)
     v4i ra[PD][LA];
@@ -399,7 +407,7 @@ bool get_splitk_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters
 template <int MT, int NTW, int WGM, int WGN, int KS, int PD, Mode MODE>
 static hipError_t launch_skinny_t(const GemmProblem &p, int splits, hipStream_t stream, std::string &config) {
     constexpr int ROWS = 16 * MT, BN = 16 * NTW, NT = 64 * WGM * WGN;
-    constexpr int NBW = BN >= 128 ? BN / 128 : 1;
+    constexpr int NBW = skinny_scale_blocks(BN);
     constexpr int STAGE = KS * (ROWS + BN) * kKBlock + KS * ROWS * 4 + ((KS * NBW * 4 + 15) / 16) * 16;
     constexpr int LDS = 2 * STAGE;
     static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -453,15 +461,23 @@ hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, 
     const int nkb = p.K / kKBlock;
     if (!skinny_eligible(p)) return hipErrorInvalidValue;
     if (p.mode == Mode::Masked) return launch_skinny_t<8, 8, 4, 2, 1, 2, Mode::Masked>(p, 1, stream, config);
-    // Dense, M <= 128.  Wide N: 128-column tiles on 8 waves (A re-read from L2
-    // once per 128 columns); narrow N: 64-column tiles on 4 waves.  Split K so
-    // that about 3/4 of the CUs get one workgroup, each split keeping at least
-    // 8 K blocks.  (Tile and split choices measured on MI355X for the decode
-    // shapes N x K = 2112 x 7168, 24576 x 1536, 7168 x 16384.)
+    // Dense, M <= 128.  Wide N: 128- or 96-column tiles (A re-read from L2
+    // once per tile), whichever leaves fewer columns per CU: 24576 columns
+    // make 256 tiles of 96 (every CU streams 96 columns) against 192 of 128
+    // (a quarter of the CUs idle).  Narrow N: 64-column tiles on 4 waves.
+    // Split K so that about 3/4 of the CUs get one workgroup, each split
+    // keeping at least 8 K blocks.  (Tile and split choices measured on
+    // MI355X for the decode shapes N x K = 2112 x 7168, 24576 x 1536,
+    // 7168 x 16384.)
     const int cus = num_cus > 0 ? num_cus : 256;
     const bool small_m = p.rows_a <= 64;
     const bool wide = p.N >= 4096;
-    const int bn = wide ? 128 : 64;
+    auto cols_per_cu = [&](int w) {
+        const int64_t t = (p.N + w - 1) / w;
+        return ((t + cus - 1) / cus) * w;
+    };
+    const bool w96 = wide && cols_per_cu(96) < cols_per_cu(128);
+    const int bn = wide ? (w96 ? 96 : 128) : 64;
     const int tiles_n = (p.N + bn - 1) / bn;
     const int target = (cus * 3) / 4;
     int splits = (target + tiles_n / 2) / tiles_n;
@@ -469,9 +485,11 @@ hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, 
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     if (small_m) {
+        if (w96) return launch_skinny_t<4, 6, 2, 3, 1, 2, Mode::Dense>(p, splits, stream, config);
         if (wide) return launch_skinny_t<4, 8, 2, 4, 1, 2, Mode::Dense>(p, splits, stream, config);
         return launch_skinny_t<4, 4, 2, 2, 1, 2, Mode::Dense>(p, splits, stream, config);
     }
+    if (w96) return launch_skinny_t<8, 6, 4, 3, 1, 2, Mode::Dense>(p, splits, stream, config);
     if (wide) return launch_skinny_t<8, 8, 4, 2, 1, 2, Mode::Dense>(p, splits, stream, config);
     return launch_skinny_t<8, 4, 2, 2, 1, 2, Mode::Dense>(p, splits, stream, config);
 }

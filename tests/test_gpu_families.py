@@ -128,3 +128,26 @@ def test_repeated_calls_leave_split_counters_clean(family):
         assert out.guards_intact()
         ref = oracle.gemm_nt(p["a"], p["sfa"], p["b"], p["sfb"], None)
         check_close(out.bits(), ref, f"{family} repeated {M}x{N}x{K} ({dg.last_config()})")
+
+
+@pytest.mark.parametrize("M,N,K,with_c", [(37, 4128, 512, True), (128, 4224, 640, False), (64, 24576, 256, True)])
+def test_skinny_96_column_tiles(M, N, K, with_c):
+    """Wide N where 96-column tiles leave fewer columns per CU than 128-column
+    ones: tiles then start inside a 128-column scale block and reach into the
+    next (tile t covers columns 96t .. 96t+95), so each wave takes the scale
+    block of its own columns.  Full compare (with an N tail at 4128)."""
+    announce(f"skinny 96-column tiles M={M} N={N} K={K} C={with_c}")
+    dg.set_kernel_family("skinny")
+    try:
+        p = dense_problem(M, N, K, seed=M * 7 + N + K, with_c=with_c)
+        out = Guarded((M, N))
+        c = dev_bf16(p["c"]) if p["c"] is not None else None
+        dg.fp8_gemm_nt(dev(p["a"]), dev(p["sfa"]), dev(p["b"]), dev(p["sfb"]), out.t, c=c)
+        torch.cuda.synchronize()
+        cfg = dg.last_config()
+    finally:
+        dg.set_kernel_family("auto")
+    assert "family=skinny" in cfg and "cols=96" in cfg, cfg
+    assert out.guards_intact()
+    ref = oracle.gemm_nt(p["a"], p["sfa"], p["b"], p["sfb"], p["c"])
+    check_close(out.bits(), ref, f"skinny 96 {M}x{N}x{K} ({cfg})")
