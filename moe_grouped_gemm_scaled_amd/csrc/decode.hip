@@ -485,7 +485,7 @@ hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, 
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     if (small_m) {
-        if (w96) return launch_skinny_t<4, 6, 2, 3, 1, 2, Mode::Dense>(p, splits, stream, config);
+        if (w96) return launch_skinny_t<4, 6, 4, 3, 1, 2, Mode::Dense>(p, splits, stream, config);
         if (wide) return launch_skinny_t<4, 8, 2, 4, 1, 2, Mode::Dense>(p, splits, stream, config);
         return launch_skinny_t<4, 4, 2, 2, 1, 2, Mode::Dense>(p, splits, stream, config);
     }
