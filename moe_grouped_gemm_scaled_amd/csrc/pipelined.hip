@@ -293,6 +293,15 @@ pipe_kernel(PipeParams p) {
     const int wm = wave / WGN, wn = wave % WGN;
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
+    // contiguous 256-row units hold one or two 128-row blocks of their expert:
+    // the waves whose rows all lie past a one-block unit skip the multiplies
+    // (those rows are never stored).  Uniform per wave; the multiply step
+    // holds no barrier and no global load.
+    bool wave_live = true;
+    if constexpr (MODE == Mode::Contig && BM == 256) {
+        const int unit_rows = (m0 + 128 < rows_a && p.idx[m0 + 128] == expert) ? 256 : 128;
+        wave_live = wm * TM < unit_rows;
+    }
 
     // ---- DMA plan.  A step's A tile is KS*BM/8 1-KB chunks: chunk c holds
     // rows 8(c / KS) .. +7 of K block c % KS.  Wave w issues chunks
@@ -589,7 +598,7 @@ pipe_kernel(PipeParams p) {
                 __builtin_amdgcn_s_waitcnt(kWaitPipe);
                 lds_barrier();
                 dma(stage_of(sc), st0 + min(j + NST - 1, nblk - 1));
-                if (j >= 0) compute(stage_of(std::integral_constant<int, (u + 1) % NST>{}));
+                if (j >= 0 && wave_live) compute(stage_of(std::integral_constant<int, (u + 1) % NST>{}));
             });
         }
     }
