@@ -27,7 +27,12 @@ E4M3 and resident; value -> TFLOP/s of 2 * H * 128 per computed logit.
 Prints ONE JSON line.  `value` is whole-job throughput: decode -> GB/s of
 algorithmic HBM traffic (activation read + codes/scales written by the
 quantiser, A + B + scales + D read/written by the GEMM); prefill and grouped
--> TFLOP/s of 2*M_valid*N*K.
+-> TFLOP/s of 2*M_valid*N*K.  `roofline` is the dominant kernels' figure:
+algorithmic units of one launch of each GEMM of the step over the sum of
+their median launch durations.  The decode run also carries `secondary`: the
+same figures for the prefill, contiguous and masked workloads, measured in
+the same process (--no-secondary skips them).  Dense decode GEMMs get their
+split-K scratch from workspaces this script allocates (zeroed once).
 """
 import argparse
 import json
@@ -130,12 +135,15 @@ def dense_jobs(cfgs, ue8m0=False, layout="nt"):
             c = torch.from_numpy(synth.normal_bf16_bits(seed, synth.STREAM_C, (M, N)).view(np.int16)).cuda()
             c = c.view(torch.bfloat16)
         d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        # split-K scratch owned here, zeroed once, shared by every launch of this
+        # job (they run in stream order); None when the shape does not split K
+        ws = dg.get_workspace(M, N, K)
 
         if layout == "nt":
-            def launch(ci, with_quant, x=x, a=a, sfa=sfa, bs=bs, sfbs=sfbs, c=c, d=d):
+            def launch(ci, with_quant, x=x, a=a, sfa=sfa, bs=bs, sfbs=sfbs, c=c, d=d, ws=ws):
                 if with_quant:
                     dg.quantize_e4m3_1x128(x, q=a, sf=sfa, ue8m0=ue8m0)
-                dg.fp8_gemm_nt(a, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c, ue8m0=ue8m0)
+                dg.fp8_gemm_nt(a, sfa, bs[ci % len(bs)], sfbs[ci % len(bs)], d, c=c, ue8m0=ue8m0, workspace=ws)
             qbytes = quant_bytes(M, K)
         else:
             dg.quantize_e4m3_1x128(x, q=a, sf=sfa)
@@ -259,10 +267,9 @@ _CAPTURE_STREAM = None
 
 
 def capture(fn):
-    """Capture fn() into a graph on one dedicated stream, after an eager call on
-    that same stream: the library's per-(device, stream) split-K workspace is
-    allocated by the eager call and reused by the captured launches (a stream
-    seen for the first time under capture would fall back to no split)."""
+    """Capture fn() into a graph on one dedicated stream, after one eager call
+    on that stream (first-call set-up such as kernel attributes happens
+    outside the capture)."""
     global _CAPTURE_STREAM
     if _CAPTURE_STREAM is None:
         _CAPTURE_STREAM = torch.cuda.Stream()
@@ -278,28 +285,31 @@ def capture(fn):
     return g
 
 
-def kernel_durations(jobs, reps=24):
-    """Average duration of one GEMM launch per job: HIP events around graph
-    replays of `reps` launches over rotating weight copies (quantiser excluded)."""
+def kernel_durations(jobs, reps=24, trials=9):
+    """Duration of one GEMM launch per job: HIP events on the capture stream
+    around graph replays of `reps` launches over rotating weight copies
+    (quantiser excluded); the median over `trials` replays, and their spread."""
     out = []
+    s = _CAPTURE_STREAM
     for j in jobs:
         def body(j=j):
             for r in range(reps):
                 j.launch(r, False)
         g = capture(body)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        best = None
-        for _ in range(5):
-            e0.record()
+        with torch.cuda.stream(s):
             g.replay()
-            e1.record()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(trials):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(s):
+                e0.record()
+                g.replay()
+                e1.record()
             e1.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            best = ms if best is None else min(best, ms)
-        out.append(best)
+            times.append(e0.elapsed_time(e1) / reps)
+        out.append((float(np.median(times)), float(min(times)), float(max(times))))
         del g
     return out
 
@@ -330,16 +340,12 @@ def measured_traffic(workload, jobs):
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(workload, jobs_meta, budget_s=15.0):
+def _decode_oracle(budget_s):
+    """The oracle (at its current thread count) on all rows and a leading
+    fraction of the columns of the six decode GEMMs plus the full activation
+    quantiser, sized to about budget_s seconds; returns the algorithmic GB/s of
+    the whole step with the GEMM time scaled by the column fraction."""
     import oracle
-    cores = oracle.num_threads()
-    if workload == "mqa":
-        return cpu_baseline_mqa(jobs_meta, budget_s)
-    if workload != "decode":
-        return None
-    total_bytes = 0
-    t_full = 0.0
-    macs_sample = 0
     cfgs = synth.DECODE
     # calibrate the oracle's multiply-add rate on a small slice
     cfg = cfgs[0]
@@ -352,6 +358,7 @@ def cpu_baseline(workload, jobs_meta, budget_s=15.0):
     rate = cfg["M"] * 64 * cfg["K"] / (time.perf_counter() - t0)
     full_macs = sum(c["M"] * c["N"] * c["K"] for c in cfgs)
     frac = min(1.0, budget_s * rate / full_macs)
+    total_bytes, t_full, macs_sample = 0, 0.0, 0
     for cfg in cfgs:
         M, N, K = cfg["M"], cfg["N"], cfg["K"]
         ns = max(128, int(N * frac) // 128 * 128)
@@ -367,11 +374,57 @@ def cpu_baseline(workload, jobs_meta, budget_s=15.0):
         t_full += tq + tg * (N / ns)
         macs_sample += M * ns * K
         total_bytes += gemm_bytes(M, N, K) + quant_bytes(M, K)
-    return {"value": total_bytes / t_full / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": (f"all rows of each of the 6 decode GEMMs x the first {frac:.3f} of their columns "
-                       f"({macs_sample / 1e9:.2f} G multiply-adds of {full_macs / 1e9:.2f} G), plus the full "
-                       f"activation quantiser; time scaled to the whole step by the column fraction"),
-            "seconds_full_step_extrapolated": t_full}
+    sample = (f"all rows of each of the 6 decode GEMMs x the first {frac:.4f} of their columns "
+              f"({macs_sample / 1e9:.2f} G multiply-adds of {full_macs / 1e9:.2f} G), plus the full "
+              f"activation quantiser; time scaled to the whole step by the column fraction")
+    return total_bytes / t_full / 1e9, t_full, sample
+
+
+def _small_oracle(reps=5):
+    """The oracle on the whole dense 128x256x512 problem (quantiser + GEMM),
+    median of `reps` runs: (GB/s of its algorithmic bytes, seconds)."""
+    import oracle
+    cfg = synth.DENSE_SMALL
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    xa = synth.normal_f32(cfg["seed"], synth.STREAM_A, (M, K))
+    xb = synth.normal_f32(cfg["seed"], synth.STREAM_B, (N, K))
+    b, sfb = oracle.quantize_128x128(xb)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        a, sfa = oracle.quantize_1x128(xa)
+        oracle.gemm_nt(a, sfa, b, sfb, None)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return (gemm_bytes(M, N, K) + quant_bytes(M, K)) / t / 1e9, t
+
+
+def cpu_baseline(workload, jobs_meta, budget_s=15.0):
+    import oracle
+    cores = oracle.num_threads()
+    if workload == "mqa":
+        return cpu_baseline_mqa(jobs_meta, budget_s)
+    if workload != "decode":
+        return None
+    gbs, t_full, sample = _decode_oracle(budget_s)
+    small_gbs, small_t = _small_oracle()
+    # the same on one thread (the survey's single-core figures for the small
+    # dense problem and the decode step), on a smaller sample
+    oracle.set_num_threads(1)
+    try:
+        gbs1, t_full1, sample1 = _decode_oracle(budget_s / 3)
+        small_gbs1, small_t1 = _small_oracle()
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle", "sample": sample,
+            "seconds_full_step_extrapolated": t_full,
+            "single_thread": {"value": gbs1, "unit": "GB/s", "cores": 1, "sample": sample1,
+                              "seconds_full_step_extrapolated": t_full1},
+            "small_dense_128x256x512": {"all_cores": {"value": small_gbs, "unit": "GB/s", "seconds": small_t,
+                                                      "cores": cores},
+                                        "single_thread": {"value": small_gbs1, "unit": "GB/s",
+                                                          "seconds": small_t1, "cores": 1},
+                                        "sample": "the whole problem: quantiser + GEMM, median of 5 runs"}}
 
 
 def cpu_baseline_mqa(meta, budget_s):
@@ -400,15 +453,162 @@ def cpu_baseline_mqa(meta, budget_s):
 
 # ---------------------------------------------------------------------------
 
+WORKLOAD_DESC = {
+    "decode": "decode-shaped dense FP8 NT GEMM, M in {64,128} x (N,K) in {(2112,7168),(24576,1536),(7168,16384)}, "
+              "1x128/128x128 block scales, C=0, bf16 D",
+    "prefill": "prefill-shaped dense FP8 NT GEMM, M=4096 x (N,K) in {(4096,7168),(7168,2048),(24576,1536)}, "
+               "C bf16, bf16 D",
+    "contiguous": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168",
+    "masked": "M-grouped masked FP8 GEMM, 16 experts x 256 rows, masked_m U[0,256], N=7168, K=2048",
+    "small": "dense FP8 NT GEMM M=128, N=256, K=512",
+    "prefill_ue8m0": "prefill-shaped dense FP8 NT GEMM, M=4096 x (N,K) in {(4096,7168),(7168,2048),(24576,1536)}, "
+                     "C bf16, bf16 D, power-of-two (UE8M0) block scales",
+    "contiguous_ue8m0": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168, "
+                        "power-of-two (UE8M0) block scales",
+    "prefill_nn": "prefill-shaped dense FP8 GEMM in the NN layout (A [M,K], B stored [K,N]), M=4096 x (N,K) in "
+                  "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
+    "prefill_tn": "prefill-shaped dense FP8 GEMM in the TN layout (A stored [K,M], B stored [K,N]), M=4096 x (N,K) in "
+                  "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
+    "prefill_tt": "prefill-shaped dense FP8 GEMM in the TT layout (A stored [K,M], B [N,K]), M=4096 x (N,K) in "
+                  "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
+    "kgrouped": "K-grouped TN contiguous FP8 GEMM (MoE weight gradient), 8 groups of the contiguous workload's "
+                "token counts padded to 128 (K_total 17408), M=7168, N=2048, 1x128 scales on both operands, "
+                "fp32 D, no C",
+    "kgrouped_ue8m0": "K-grouped TN contiguous FP8 GEMM (MoE weight gradient), 8 groups of the contiguous "
+                      "workload's token counts padded to 128 (K_total 17408), M=7168, N=2048, power-of-two "
+                      "(UE8M0) 1x128 scales on both operands, fp32 D, no C",
+    "mqa": "FP8 MQA logits (non-paged, clean_logits): 4096 query tokens x 64 heads x 128 against 8192 keys, "
+           "causal ranges, fp32 logits [4096, 8192]",
+}
+
+WORKLOADS = list(WORKLOAD_DESC)
+
+
+def build_jobs(workload):
+    """(jobs, bound, meta) of a workload."""
+    meta = {}
+    if workload == "decode":
+        return dense_jobs(synth.DECODE), "hbm", meta
+    if workload == "prefill":
+        return dense_jobs(synth.PREFILL), "mfma", meta
+    if workload == "prefill_ue8m0":
+        return dense_jobs(synth.PREFILL, ue8m0=True), "mfma", meta
+    if workload in ("prefill_nn", "prefill_tn", "prefill_tt"):
+        return dense_jobs(synth.PREFILL, layout=workload[-2:]), "mfma", meta
+    if workload == "small":
+        return dense_jobs([synth.DENSE_SMALL]), "hbm", meta
+    if workload in ("contiguous", "contiguous_ue8m0"):
+        jobs, meta = contiguous_jobs(ue8m0=workload.endswith("_ue8m0"))
+        return jobs, "mfma", meta
+    if workload in ("kgrouped", "kgrouped_ue8m0"):
+        jobs, meta = kgrouped_jobs(ue8m0=workload.endswith("_ue8m0"))
+        return jobs, "mfma", meta
+    if workload == "mqa":
+        jobs, meta = mqa_jobs()
+        return jobs, "mfma", meta
+    jobs, meta = masked_jobs()
+    return jobs, "hbm", meta
+
+
+def step_kind(workload):
+    if workload == "mqa":
+        return "one fp8_mqa_logits call, inputs resident"
+    if workload[-3:] in ("_nn", "_tn", "_tt") or workload.startswith("kgrouped"):
+        return "one GEMM per shape, operands quantised and laid out beforehand"
+    return "activation quantiser + GEMM per shape; weights pre-quantised"
+
+
+def run_workload(workload, steps, warmup):
+    """Times one workload: returns its measured figures (value, roofline,
+    per-GEMM durations) and its job metadata."""
+    jobs, bound, meta = build_jobs(workload)
+    log(f"workload {workload}: {[j.name for j in jobs]}, copies {[j.copies for j in jobs]}")
+
+    # two graphs: the W warm-up steps and the K timed steps, each captured as
+    # one graph of consecutive steps (step s uses weight copy s of every job),
+    # so that a replay boundary never sits between two timed steps
+    def steps_fn(first, count):
+        def fn():
+            for s in range(first, first + count):
+                for j in jobs:
+                    j.launch(s, True)
+        return fn
+
+    warm_graph = capture(steps_fn(0, warmup)) if warmup > 0 else None
+    timed_graph = capture(steps_fn(warmup, steps))
+    configs = []
+    with torch.cuda.stream(_CAPTURE_STREAM):       # the stream the graphs were captured on
+        for j in jobs:
+            j.launch(0, False)
+            configs.append(dg.last_config())
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(_CAPTURE_STREAM):
+        if warm_graph is not None:
+            warm_graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        timed_graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / steps
+    del warm_graph, timed_graph
+
+    kd = kernel_durations(jobs)
+    kms = [k[0] for k in kd]                       # medians
+    step_bytes = sum(j.bytes_gemm + j.bytes_quant for j in jobs)
+    step_flops = sum(j.flops for j in jobs)
+    gemm_bytes_total = sum(j.bytes_gemm for j in jobs)
+    gemm_time_s = sum(kms) / 1e3
+    per_job = [{"name": j.name, "gemm_us": round(k[0] * 1e3, 3),
+                "gemm_us_min_max": [round(k[1] * 1e3, 3), round(k[2] * 1e3, 3)],
+                "gemm_GBps": round(j.bytes_gemm / (k[0] / 1e3) / 1e9, 1),
+                "gemm_TFLOPs": round(j.flops / (k[0] / 1e3) / 1e12, 1), "config": cfg}
+               for j, k, cfg in zip(jobs, kd, configs)]
+
+    traffic = measured_traffic(workload, jobs)
+    if bound == "hbm":
+        value = step_bytes / (ms_step / 1e3) / 1e9
+        unit = "GB/s"
+        achieved = gemm_bytes_total / gemm_time_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        value = step_flops / (ms_step / 1e3) / 1e12
+        unit = "TFLOP/s"
+        achieved = step_flops / gemm_time_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+    # bytes the traffic figure compares with: the algorithmic bytes of the same launches
+    roof["algorithmic_bytes"] = round(gemm_bytes_total)
+    res = {"workload": workload, "value": round(value, 2), "unit": unit, "steps": steps, "warmup": warmup,
+           "ms_per_step": round(ms_step, 5), "roofline": roof,
+           "frac_of_peak_step": round(value / (HBM_PEAK_GBS if bound == "hbm" else FP8_PEAK_TFLOPS), 4),
+           "per_gemm": per_job}
+    del jobs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, meta
+
+
+def data_desc(workload):
+    if workload == "mqa":
+        return ("synthetic: seeded uniformly random e4m3 codes for q and kv, kv_scale 2^-9 (1+U[0,1)), "
+                "weights N(0,1)/8")
+    return ("synthetic: seeded N(0,1) fp32, quantised to e4m3 with 1x128 / 128x128 fp32 scales"
+            + (" rounded up to powers of two (UE8M0)" if workload.endswith("_ue8m0") else ""))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "contiguous", "masked", "small", "prefill_ue8m0", "contiguous_ue8m0",
-                             "mqa", "prefill_nn", "prefill_tn", "prefill_tt", "kgrouped", "kgrouped_ue8m0"])
+    ap.add_argument("--workload", default="decode", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="decode only: skip the prefill, contiguous and masked figures in `secondary`")
+    ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB each (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -430,151 +630,44 @@ def main():
         return
     dg.lib()
 
-    meta = {}
-    if args.workload == "decode":
-        jobs = dense_jobs(synth.DECODE)
-        bound = "hbm"
-    elif args.workload == "prefill":
-        jobs = dense_jobs(synth.PREFILL)
-        bound = "mfma"
-    elif args.workload == "prefill_ue8m0":
-        jobs = dense_jobs(synth.PREFILL, ue8m0=True)
-        bound = "mfma"
-    elif args.workload == "contiguous_ue8m0":
-        jobs, meta = contiguous_jobs(ue8m0=True)
-        bound = "mfma"
-    elif args.workload in ("prefill_nn", "prefill_tn", "prefill_tt"):
-        jobs = dense_jobs(synth.PREFILL, layout=args.workload[-2:])
-        bound = "mfma"
-    elif args.workload in ("kgrouped", "kgrouped_ue8m0"):
-        jobs, meta = kgrouped_jobs(ue8m0=args.workload.endswith("_ue8m0"))
-        bound = "mfma"
-    elif args.workload == "mqa":
-        jobs, meta = mqa_jobs()
-        bound = "mfma"
-    elif args.workload == "small":
-        jobs = dense_jobs([synth.DENSE_SMALL])
-        bound = "hbm"
-    elif args.workload == "contiguous":
-        jobs, meta = contiguous_jobs()
-        bound = "mfma"
-    else:
-        jobs, meta = masked_jobs()
-        bound = "hbm"
-    log(f"workload {args.workload}: {[j.name for j in jobs]}, copies {[j.copies for j in jobs]}")
+    res, meta = run_workload(args.workload, args.steps, args.warmup)
 
-    # two graphs: the W warm-up steps and the K timed steps, each captured as
-    # one graph of consecutive steps (step s uses weight copy s of every job),
-    # so that a replay boundary never sits between two timed steps
-    def steps_fn(first, count):
-        def fn():
-            for s in range(first, first + count):
-                for j in jobs:
-                    j.launch(s, True)
-        return fn
-
-    warm_graph = capture(steps_fn(0, args.warmup)) if args.warmup > 0 else None
-    timed_graph = capture(steps_fn(args.warmup, args.steps))
-    configs = []
-    with torch.cuda.stream(_CAPTURE_STREAM):       # the stream the graphs were captured on
-        for j in jobs:
-            j.launch(0, False)
-            configs.append(dg.last_config())
-    torch.cuda.synchronize()
-
-    if warm_graph is not None:
-        warm_graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    timed_graph.replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-
-    kms = kernel_durations(jobs)
-    step_bytes = sum(j.bytes_gemm + j.bytes_quant for j in jobs)
-    step_flops = sum(j.flops for j in jobs)
-    gemm_bytes_total = sum(j.bytes_gemm for j in jobs)
-    gemm_time_s = sum(kms) / 1e3
-    per_job = [{"name": j.name, "gemm_us": round(k * 1e3, 3),
-                "gemm_GBps": round(j.bytes_gemm / (k / 1e3) / 1e9, 1),
-                "gemm_TFLOPs": round(j.flops / (k / 1e3) / 1e12, 1), "config": cfg}
-               for j, k, cfg in zip(jobs, kms, configs)]
-
-    traffic = measured_traffic(args.workload, jobs)
-    if bound == "hbm":
-        value = step_bytes / (ms_step / 1e3) / 1e9
-        unit = "GB/s"
-        achieved = gemm_bytes_total / gemm_time_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        value = step_flops / (ms_step / 1e3) / 1e12
-        unit = "TFLOP/s"
-        achieved = step_flops / gemm_time_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
-    # bytes the traffic figure compares with: the algorithmic bytes of the same launches
-    roof["algorithmic_bytes"] = round(gemm_bytes_total)
+    # the other half of the metric, from the same process: the compute-bound
+    # prefill and contiguous workloads and the HBM-bound masked one
+    secondary = []
+    if args.workload == "decode" and not args.no_secondary:
+        for w in ("prefill", "contiguous", "masked"):
+            r, m = run_workload(w, args.secondary_steps, min(args.warmup, 3))
+            r["config"] = {"workload": WORKLOAD_DESC[w], "step": step_kind(w), "graph_replay": True,
+                           **({"layout": m} if m else {})}
+            r["data"] = data_desc(w)
+            secondary.append(r)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
         cpu = cpu_baseline(args.workload, meta)
 
-    workload_desc = {
-        "decode": "decode-shaped dense FP8 NT GEMM, M in {64,128} x (N,K) in {(2112,7168),(24576,1536),(7168,16384)}, "
-                  "1x128/128x128 block scales, C=0, bf16 D",
-        "prefill": "prefill-shaped dense FP8 NT GEMM, M=4096 x (N,K) in {(4096,7168),(7168,2048),(24576,1536)}, "
-                   "C bf16, bf16 D",
-        "contiguous": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168",
-        "masked": "M-grouped masked FP8 GEMM, 16 experts x 256 rows, masked_m U[0,256], N=7168, K=2048",
-        "small": "dense FP8 NT GEMM M=128, N=256, K=512",
-        "prefill_ue8m0": "prefill-shaped dense FP8 NT GEMM, M=4096 x (N,K) in {(4096,7168),(7168,2048),(24576,1536)}, "
-                         "C bf16, bf16 D, power-of-two (UE8M0) block scales",
-        "contiguous_ue8m0": "M-grouped contiguous FP8 GEMM, 8 experts, counts U[1,4096] padded to 128, N=4096, K=7168, "
-                            "power-of-two (UE8M0) block scales",
-        "prefill_nn": "prefill-shaped dense FP8 GEMM in the NN layout (A [M,K], B stored [K,N]), M=4096 x (N,K) in "
-                      "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
-        "prefill_tn": "prefill-shaped dense FP8 GEMM in the TN layout (A stored [K,M], B stored [K,N]), M=4096 x (N,K) in "
-                      "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
-        "prefill_tt": "prefill-shaped dense FP8 GEMM in the TT layout (A stored [K,M], B [N,K]), M=4096 x (N,K) in "
-                      "{(4096,7168),(7168,2048),(24576,1536)}, C bf16, bf16 D",
-        "kgrouped": "K-grouped TN contiguous FP8 GEMM (MoE weight gradient), 8 groups of the contiguous workload's "
-                    "token counts padded to 128 (K_total 17408), M=7168, N=2048, 1x128 scales on both operands, "
-                    "fp32 D, no C",
-        "kgrouped_ue8m0": "K-grouped TN contiguous FP8 GEMM (MoE weight gradient), 8 groups of the contiguous "
-                          "workload's token counts padded to 128 (K_total 17408), M=7168, N=2048, power-of-two "
-                          "(UE8M0) 1x128 scales on both operands, fp32 D, no C",
-        "mqa": "FP8 MQA logits (non-paged, clean_logits): 4096 query tokens x 64 heads x 128 against 8192 keys, "
-               "causal ranges, fp32 logits [4096, 8192]",
-    }[args.workload]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
-        "unit": unit,
+        "value": res["value"],
+        "unit": res["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3",
-        "data": ("synthetic: seeded uniformly random e4m3 codes for q and kv, kv_scale 2^-9 (1+U[0,1)), "
-                 "weights N(0,1)/8" if args.workload == "mqa" else
-                 "synthetic: seeded N(0,1) fp32, quantised to e4m3 with 1x128 / 128x128 fp32 scales"
-                 + (" rounded up to powers of two (UE8M0)" if args.workload.endswith("_ue8m0") else "")),
-        "config": {"workload": workload_desc,
-                   "step": ("one fp8_mqa_logits call, inputs resident" if args.workload == "mqa" else
-                            "one GEMM per shape, operands quantised and laid out beforehand"
-                            if args.workload[-3:] in ("_nn", "_tn", "_tt") or args.workload.startswith("kgrouped") else
-                            "activation quantiser + GEMM per shape; weights pre-quantised"),
+        "data": data_desc(args.workload),
+        "config": {"workload": WORKLOAD_DESC[args.workload], "step": step_kind(args.workload),
                    "graph_replay": True, **({"layout": meta} if meta else {})},
-        "roofline": roof,
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
-        "frac_of_peak_step": round(value / (HBM_PEAK_GBS if bound == "hbm" else FP8_PEAK_TFLOPS), 4),
-        "per_gemm": per_job,
+        "frac_of_peak_step": res["frac_of_peak_step"],
+        "per_gemm": res["per_gemm"],
+        "secondary": secondary,
     }
     print(json.dumps(out), flush=True)
 

@@ -32,16 +32,18 @@
  *  - K must be a positive multiple of 128.  M and N may be any positive size
  *    (partial row and column tiles are handled), except where an operand is
  *    stored MN-major (multiples of 16).
- *  - Dense calls with a small M use split-K: they keep an internal fp32
- *    workspace per device and stream (allocated on first use, grown when a
- *    larger problem arrives, freed at process exit).  Calls on one stream
- *    are ordered; calls on different streams use different workspaces.
- *  - Thread-safe: the only global settings are the CU cap and the last-config
- *    string (which is per thread).
+ *  - The library allocates no device memory and never synchronises.  Dense
+ *    calls with a small M run fastest with K split over several workgroups,
+ *    which needs scratch memory: the *_ws entry points take it from the
+ *    caller (size from dg_get_workspace_size), the others run without
+ *    split-K.
+ *  - Thread-safe.  Process-wide settings: the CU cap only.  Per thread: the
+ *    kernel-family setting and the last-config string.
  */
 #ifndef DG_H
 #define DG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -75,6 +77,47 @@ int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa,
                    const uint8_t *b, const float *sfb,
                    const uint16_t *c, uint16_t *d,
                    int M, int N, int K, void *stream);
+
+/*
+ * The dense GEMM with caller-provided split-K scratch.  Same arguments,
+ * results and errors as dg_fp8_gemm_nt (and dg_fp8_gemm_nt_ue8m0), plus:
+ *   workspace        device memory, 16-byte aligned, or NULL (then K is
+ *                    never split: the dg_fp8_gemm_nt path);
+ *   workspace_bytes  its size; at least dg_get_workspace_size(M, N, K) for
+ *                    the configuration the call chooses (DG_ERR_ARG
+ *                    otherwise, before anything is launched).
+ * Layout: the workspace starts with one int32 arrival counter per output
+ * tile, which must be ZERO when a call starts; every call that completes
+ * leaves them zero again, so memory zeroed once (hipMemset, torch.zeros)
+ * serves any number of calls in stream order, eager or captured in a graph.
+ * The rest holds the fp32 partial tiles of the K splits.  The caller owns
+ * the workspace; it must stay allocated until the call's work completes, and
+ * two calls that may run at the same time (other streams, concurrently
+ * replayed graphs) need two workspaces.  The partials of the splits are
+ * added in split order, so the result does not depend on the order in which
+ * the splits finish.
+ */
+int dg_fp8_gemm_nt_ws(const uint8_t *a, const float *sfa, int ld_sfa,
+                      const uint8_t *b, const float *sfb,
+                      const uint16_t *c, uint16_t *d,
+                      int M, int N, int K,
+                      void *workspace, size_t workspace_bytes, void *stream);
+int dg_fp8_gemm_nt_ue8m0_ws(const uint8_t *a, const float *sfa, int ld_sfa,
+                            const uint8_t *b, const float *sfb,
+                            const uint16_t *c, uint16_t *d,
+                            int M, int N, int K,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes for dg_fp8_gemm_nt_ws and dg_fp8_gemm_nt_ue8m0_ws on an
+ * M x N x K problem on the current device, with the calling thread's kernel
+ * family setting and the CU cap in force (0: the problem is not split).
+ * Negative dg_status on error: DG_ERR_SHAPE (M, N < 1; K), DG_ERR_HIP or
+ * DG_ERR_UNSUPPORTED (no usable device).  The pages' library keeps such
+ * buffers itself; here the caller owns all memory, so that every call is
+ * asynchronous and can be captured into a graph.
+ */
+int64_t dg_get_workspace_size(int M, int N, int K);
 
 /*
  * The other memory layouts of the dense GEMM ("DeepGEMM" README summary,
@@ -300,40 +343,49 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t *a, const float *sfa,
                                         const int32_t *ks, const float *c, float *d,
                                         int M, int N, int K, int G, void *stream);
 
-/* Row alignment of expert segments in the contiguous layout (128).  The
- * setter accepts only 128 and returns DG_ERR_ARG otherwise. ("Utilities and
- * environment variables" section.) */
+/* Row alignment of expert segments in the contiguous layout (128): the
+ * set_/get_mk_alignment_for_contiguous_layout utilities of the "DeepGEMM"
+ * README summary, section "Utilities and environment variables".  The
+ * setter accepts only 128 and returns DG_ERR_ARG otherwise. */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 int dg_set_mk_alignment_for_contiguous_layout(int alignment);
 
 /* Leading dimension for a transposed scale array over mn rows: round_up(mn, 4)
- * (16-byte aligned columns, the analogue of the TMA-aligned size). */
+ * (16-byte aligned columns).  The analogue of get_tma_aligned_size in the
+ * same section (the LHS scales must be stored transposed and aligned,
+ * section "GEMM interface and layout constraints"). */
 int dg_get_sf_aligned_size(int mn);
 
-/* Cap on the number of compute units the tile scheduler plans for (the
- * analogue of set_num_sms).  n >= 1 sets the cap, n == 0 restores the
- * device's CU count; negative -> DG_ERR_ARG.  get returns the cap in force
- * (the device's CU count when none is set, or a negative dg_status when no
- * device can be queried). */
+/* Cap on the number of compute units the tile scheduler plans for: the
+ * analogue of set_num_sms / get_num_sms in the same section.  n >= 1 sets
+ * the cap, n == 0 restores the device's CU count; negative -> DG_ERR_ARG.
+ * get returns the cap in force (the device's CU count when none is set, or
+ * a negative dg_status when no device can be queried).  Process-wide. */
 int dg_set_num_cus(int n);
 int dg_get_num_cus(void);
 
-/* Kernel family used by the GEMM entry points, for tuning and testing:
- * "auto" (the default: chosen per problem), "pipe", "persist", "skinny" or
- * "tiled".  A family that cannot take a problem falls back to the automatic
- * choice; results are the same whichever family runs (within the documented
- * tolerance).  The initial value comes from the environment variable
+/* Kernel family used by the GEMM entry points called from this thread, for
+ * tuning and testing: "auto" (the default: chosen per problem), "pipe",
+ * "persist", "skinny" or "tiled".  Not on the pages (whose JIT picks one
+ * kernel per shape, "Utilities and environment variables"); here every
+ * family stays reachable so each can be tested.  A family that cannot take a
+ * problem falls back to the automatic choice; results agree to the
+ * documented tolerance whichever family runs, but are not bit-identical
+ * across families.  Every thread starts from the environment variable
  * DG_KERNEL_FAMILY.  set returns DG_ERR_NULL or DG_ERR_ARG for a NULL or
- * unknown name; get returns the name in force (process-wide setting). */
+ * unknown name; get returns the calling thread's setting. */
 int dg_set_kernel_family(const char *name);
 const char *dg_get_kernel_family(void);
 
-/* Static string for a status code. */
+/* Static string for a status code.  The pages' Python interface raises
+ * exceptions; a C ABI returns codes instead, and this names them. */
 const char *dg_status_string(int status);
 
 /* Description of the kernel configuration chosen by this thread's last GEMM
  * call (family, tile, grid, split).  Also printed to stderr for every call
- * when the environment variable DG_PRINT_CONFIGS is set to a non-zero value. */
+ * when the environment variable DG_PRINT_CONFIGS is set to a non-zero value:
+ * the DG_PRINT_CONFIGS variable of the same section, which prints the config
+ * chosen for each shape. */
 const char *dg_last_config(void);
 
 #ifdef __cplusplus

@@ -28,6 +28,13 @@ EXPORTS = {
     # name: (restype, argtypes)
     "dg_fp8_gemm_nt": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                   ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_fp8_gemm_nt_ws": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                     ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_size_t,
+                                     ct.c_void_p]),
+    "dg_fp8_gemm_nt_ue8m0_ws": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p,
+                                           ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
+                                           ct.c_size_t, ct.c_void_p]),
+    "dg_get_workspace_size": (ct.c_int64, [ct.c_int, ct.c_int, ct.c_int]),
     "dg_m_grouped_fp8_gemm_nt_contiguous": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                                        ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int,
                                                        ct.c_int, ct.c_int, ct.c_void_p]),
@@ -146,18 +153,47 @@ def _name(base: str, ue8m0: bool) -> str:
     return base + "_ue8m0" if ue8m0 else base
 
 
-def fp8_gemm_nt(a, sfa, b, sfb, d, c=None, ue8m0=False):
+def get_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of split-K scratch dg_fp8_gemm_nt_ws needs for M x N x K on the current device (0: no split)."""
+    v = lib().dg_get_workspace_size(int(M), int(N), int(K))
+    if v < 0:
+        raise DGError(int(v), "dg_get_workspace_size")
+    return int(v)
+
+
+def get_workspace(M: int, N: int, K: int, device=None):
+    """A zero-filled uint8 device tensor of get_workspace_size(M, N, K) bytes (None when the problem does
+    not split K).  It may serve any number of fp8_gemm_nt calls in stream order; calls that can run at
+    the same time (other streams, graphs replayed concurrently) each need their own."""
+    n = get_workspace_size(M, N, K)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device if device is not None else "cuda")
+
+
+def fp8_gemm_nt(a, sfa, b, sfb, d, c=None, ue8m0=False, workspace="auto"):
     """D = C + A . B^T.  a[M,K], sfa[K/128, ld_sfa], b[N,K], sfb[ceil(N/128), K/128], d/c[M,N] bf16.
-    ue8m0: every scale is a power of two (dg_fp8_gemm_nt_ue8m0)."""
+    ue8m0: every scale is a power of two (dg_fp8_gemm_nt_ue8m0[_ws]).
+    workspace: a zeroed uint8 device tensor from get_workspace() (dg_fp8_gemm_nt_ws); None runs without
+    split-K (dg_fp8_gemm_nt); "auto" takes a fresh zeroed one from torch's allocator for this call."""
     M, K = a.shape
     N = b.shape[0]
     if sfa.dim() != 2 or sfa.shape[0] != K // 128:
         raise ValueError(f"sfa: shape {tuple(sfa.shape)}, expected [K/128={K // 128}, ld_sfa]")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace {workspace!r}")
+        workspace = get_workspace(M, N, K, d.device)
     args = (_ptr(a, _FP8, "a", (M, K)), _ptr(sfa, torch.float32, "sfa"), int(sfa.shape[1]),
             _ptr(b, _FP8, "b", (N, K)), _ptr(sfb, torch.float32, "sfb", (ceil_div(N, 128), K // 128)),
-            _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
-    name = _name("dg_fp8_gemm_nt", ue8m0)
-    _check(getattr(lib(), name)(*args), name)
+            _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K)
+    if workspace is None:
+        name = _name("dg_fp8_gemm_nt", ue8m0)
+        _check(getattr(lib(), name)(*args, _stream(d)), name)
+    else:
+        name = "dg_fp8_gemm_nt_ue8m0_ws" if ue8m0 else "dg_fp8_gemm_nt_ws"
+        ws = _ptr(workspace, torch.uint8, "workspace")
+        _check(getattr(lib(), name)(*args, ws, int(workspace.numel()), _stream(d)), name)
     return d
 
 
@@ -299,7 +335,7 @@ def get_num_cus() -> int:
 
 
 def set_kernel_family(name: str):
-    """Kernel family of the GEMM entry points: auto, pipe, persist, skinny or tiled."""
+    """Kernel family of the GEMM entry points called from this thread: auto, pipe, persist, skinny or tiled."""
     _check(lib().dg_set_kernel_family(name.encode()), "dg_set_kernel_family")
 
 

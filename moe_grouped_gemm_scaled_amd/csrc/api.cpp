@@ -50,10 +50,28 @@ int current_device(int &dev, int &cus) {
     return DG_OK;
 }
 
+// Scratch bytes the configuration chosen for p needs (0: it does not split K).
+int plan_scratch(const dg::GemmProblem &p, int cus, size_t &need) {
+    dg::GemmProblem q = p;
+    q.ws = nullptr;
+    q.ws_bytes = 0;
+    need = 0;
+    q.plan = &need;
+    std::string cfg;
+    return dg::launch_gemm(q, cus, nullptr, cfg) == hipSuccess ? DG_OK : DG_ERR_ARG;
+}
+
 int run_gemm(const dg::GemmProblem &p, void *stream) {
     int dev = 0, cus = 0;
     const int st = current_device(dev, cus);
     if (st != DG_OK) return st;
+    if (p.ws) {
+        // a scratch that is given must hold what the chosen configuration needs
+        size_t need = 0;
+        const int ps = plan_scratch(p, cus, need);
+        if (ps != DG_OK) return ps;
+        if (p.ws_bytes < need) return DG_ERR_ARG;
+    }
     std::string cfg;
     const hipError_t err = dg::launch_gemm(p, cus, static_cast<hipStream_t>(stream), cfg);
     t_last_config = cfg;
@@ -68,14 +86,17 @@ int check_k(int K) { return (K < 128 || K % 128 != 0) ? DG_ERR_SHAPE : DG_OK; }
 extern "C" {
 
 static int gemm_nt_impl(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
-                        const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream, bool ue8m0) {
+                        const uint16_t *c, uint16_t *d, int M, int N, int K, void *workspace,
+                        size_t workspace_bytes, void *stream, bool ue8m0) {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_NULL;
     if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (ld_sfa < M || ld_sfa % 4 != 0) return DG_ERR_ALIGN;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
-        (c && !aligned16(c)))
+        (c && !aligned16(c)) || (workspace && !aligned16(workspace)))
         return DG_ERR_ALIGN;
     dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, ue8m0};
+    p.ws = workspace;
+    p.ws_bytes = workspace ? workspace_bytes : 0;
     return run_gemm(p, stream);
 }
 
@@ -185,12 +206,42 @@ int dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(const uint8_t *a, const float *sfa
 
 int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                    const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
-    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false);
+    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, nullptr, 0, stream, false);
 }
 
 int dg_fp8_gemm_nt_ue8m0(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                          const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
-    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, true);
+    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, nullptr, 0, stream, true);
+}
+
+int dg_fp8_gemm_nt_ws(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                      const uint16_t *c, uint16_t *d, int M, int N, int K, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, workspace, workspace_bytes, stream, false);
+}
+
+int dg_fp8_gemm_nt_ue8m0_ws(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                            const uint16_t *c, uint16_t *d, int M, int N, int K, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, workspace, workspace_bytes, stream, true);
+}
+
+int64_t dg_get_workspace_size(int M, int N, int K) {
+    if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) return st;
+    // the largest need over both scale forms (the same tiles and splits today)
+    size_t need = 0;
+    for (int ue = 0; ue < 2; ++ue) {
+        dg::GemmProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K,
+                          (M + 3) / 4 * 4, 1, dg::Mode::Dense, 0, ue != 0};
+        size_t n = 0;
+        const int ps = plan_scratch(p, cus, n);
+        if (ps != DG_OK) return ps;
+        if (n > need) need = n;
+    }
+    return (int64_t)need;
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
@@ -313,13 +364,11 @@ int dg_set_kernel_family(const char *name) {
     if (!name) return DG_ERR_NULL;
     const int f = dg::kernel_family_from_name(name);
     if (f < 0) return DG_ERR_ARG;
-    dg::kernel_family_setting().store(f, std::memory_order_relaxed);
+    dg::kernel_family_setting() = f;
     return DG_OK;
 }
 
-const char *dg_get_kernel_family(void) {
-    return dg::kernel_family_name(dg::kernel_family_setting().load(std::memory_order_relaxed));
-}
+const char *dg_get_kernel_family(void) { return dg::kernel_family_name(dg::kernel_family_setting()); }
 
 const char *dg_status_string(int status) {
     switch (status) {

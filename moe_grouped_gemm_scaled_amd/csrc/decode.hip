@@ -31,9 +31,6 @@
 #include <stdio.h>
 
 #include <atomic>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "dg_device.h"
 #include "dg_internal.h"
@@ -355,55 +352,6 @@ skinny_kernel(SkinnyParams p) {
     });
 }
 
-// ---------------------------------------------------------------------------
-// split-K workspace: one per (device, stream), grown on demand; counters are
-// zeroed once at allocation and left zeroed by every completed call.
-// ---------------------------------------------------------------------------
-
-namespace {
-struct Workspace {
-    float *ws = nullptr;
-    int *counters = nullptr;
-    size_t ws_bytes = 0;
-    size_t n_counters = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-}  // namespace
-
-// Returns false when no large-enough workspace exists and none may be
-// allocated now (the stream is being captured into a graph).
-bool get_splitk_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters, float **ws, int **counters) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return false;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &w = g_ws[{dev, stream}];
-    if (w.ws_bytes < ws_bytes || w.n_counters < n_counters) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
-        // the old buffers may still be in use by queued work on this stream
-        if (hipStreamSynchronize(stream) != hipSuccess) return false;
-        if (w.ws) (void)hipFree(w.ws);
-        if (w.counters) (void)hipFree(w.counters);
-        w = Workspace{};
-        const size_t nb = ws_bytes > (16u << 20) ? ws_bytes : (16u << 20);
-        const size_t nc = n_counters > 65536 ? n_counters : 65536;
-        if (hipMalloc(&w.ws, nb) != hipSuccess) return false;
-        if (hipMalloc(&w.counters, nc * sizeof(int)) != hipSuccess) {
-            (void)hipFree(w.ws);
-            w.ws = nullptr;
-            return false;
-        }
-        // on the stream itself, so that the zeroing precedes the stream's next kernels
-        if (hipMemsetAsync(w.counters, 0, nc * sizeof(int), stream) != hipSuccess) return false;
-        w.ws_bytes = nb;
-        w.n_counters = nc;
-    }
-    *ws = w.ws;
-    *counters = w.counters;
-    return true;
-}
-
 template <int MT, int NTW, int WGM, int WGN, int KS, int PD, Mode MODE>
 static hipError_t launch_skinny_t(const GemmProblem &p, int splits, hipStream_t stream, std::string &config) {
     constexpr int ROWS = 16 * MT, BN = 16 * NTW, NT = 64 * WGM * WGN;
@@ -411,16 +359,6 @@ static hipError_t launch_skinny_t(const GemmProblem &p, int splits, hipStream_t 
     constexpr int STAGE = KS * (ROWS + BN) * kKBlock + KS * ROWS * 4 + ((KS * NBW * 4 + 15) / 16) * 16;
     constexpr int LDS = 2 * STAGE;
     static_assert(LDS <= 160 * 1024, "LDS budget");
-    // raise the dynamic LDS limit once per device (idempotent, so a race is benign)
-    static std::atomic<unsigned long long> attr_set{0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!(attr_set.load(std::memory_order_relaxed) & (1ull << dev))) {
-        const hipError_t e = hipFuncSetAttribute((const void *)skinny_kernel<MT, NTW, WGM, WGN, KS, PD, MODE>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e != hipSuccess) return e;
-        attr_set.fetch_or(1ull << dev, std::memory_order_relaxed);
-    }
     SkinnyParams k;
     k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.d = p.d;
     k.masked_m = p.idx;
@@ -436,7 +374,7 @@ static hipError_t launch_skinny_t(const GemmProblem &p, int splits, hipStream_t 
     if (splits > 1) {
         const size_t per = (size_t)ROWS * BN * sizeof(float);
         if ((int64_t)splits * ROWS * BN * 4 >= ((int64_t)1 << 31) ||
-            !get_splitk_workspace(stream, per * tiles * splits, (size_t)tiles, &k.ws, &k.counters))
+            !take_splitk_scratch(p, per * tiles * splits, (size_t)tiles, &k.ws, &k.counters))
             splits = 1;
     }
     k.splits = splits;
@@ -446,6 +384,17 @@ static hipError_t launch_skinny_t(const GemmProblem &p, int splits, hipStream_t 
     snprintf(buf, sizeof buf, "family=skinny mode=%d rows=%d cols=%d waves=%dx%d ks=%d pd=%d splits=%d grid=%lld",
              (int)MODE, ROWS, BN, WGM, WGN, KS, PD, splits, (long long)grid);
     config = buf;
+    if (p.plan) return hipSuccess;
+    // raise the dynamic LDS limit once per device (idempotent, so a race is benign)
+    static std::atomic<unsigned long long> attr_set{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!(attr_set.load(std::memory_order_relaxed) & (1ull << dev))) {
+        const hipError_t e = hipFuncSetAttribute((const void *)skinny_kernel<MT, NTW, WGM, WGN, KS, PD, MODE>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess) return e;
+        attr_set.fetch_or(1ull << dev, std::memory_order_relaxed);
+    }
     hipLaunchKernelGGL((skinny_kernel<MT, NTW, WGM, WGN, KS, PD, MODE>), dim3((unsigned)grid), dim3(NT), LDS, stream,
                        k);
     return hipGetLastError();

@@ -4,7 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
+#include <stddef.h>
+
 #include <string>
 
 namespace dg {
@@ -51,7 +52,43 @@ struct GemmProblem {
     // K-grouped only: fp32 C (or NULL) and D
     const float *c32 = nullptr;
     float *d32 = nullptr;
+    // split-K scratch brought in by the caller (dense calls only; NULL: the
+    // launchers run without split-K).  Layout: the int32 arrival counters
+    // first (the region rounded up to 256 bytes), then the fp32 partials.
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    // planning: when set, the launchers take the configuration they would
+    // take with a large enough scratch, store the scratch bytes it needs
+    // here, and launch nothing
+    size_t *plan = nullptr;
 };
+
+// Bytes of split-K scratch for `partial_bytes` of fp32 partials and
+// `n_counters` arrival counters (laid out as described above).
+constexpr size_t splitk_counter_bytes(size_t n_counters) { return (n_counters * 4 + 255) / 256 * 256; }
+constexpr size_t splitk_scratch_bytes(size_t partial_bytes, size_t n_counters) {
+    return splitk_counter_bytes(n_counters) + partial_bytes;
+}
+
+// The split-K scratch of a launch.  Planning: records the need in *p.plan and
+// grants (the launcher then returns before launching).  Otherwise grants the
+// caller's scratch when it holds `partial_bytes` of partials and
+// `n_counters` counters, and declines (run without split-K) when there is
+// none or it is too small.
+inline bool take_splitk_scratch(const GemmProblem &p, size_t partial_bytes, size_t n_counters, float **ws,
+                                int **counters) {
+    const size_t need = splitk_scratch_bytes(partial_bytes, n_counters);
+    *ws = nullptr;
+    *counters = nullptr;
+    if (p.plan) {
+        if (need > *p.plan) *p.plan = need;
+        return true;
+    }
+    if (!p.ws || p.ws_bytes < need) return false;
+    *counters = static_cast<int *>(p.ws);
+    *ws = reinterpret_cast<float *>(static_cast<char *>(p.ws) + splitk_counter_bytes(n_counters));
+    return true;
+}
 
 // Skinny-M family: dense with M <= 128, and the masked layout; needs K >= 256
 // and every operand below 2 GB (32-bit buffer offsets).
@@ -69,17 +106,10 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
 bool persist_eligible(const GemmProblem &p);
 hipError_t launch_persist(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
 
-// Split-K workspace of the calling device for `stream`: at least `ws_bytes`
-// of fp32 partials and `n_counters` zeroed arrival counters, grown on demand
-// (completed calls leave the counters zeroed).  Returns false when none large
-// enough exists and none may be allocated now (the stream is being captured
-// into a graph); the caller then runs without split-K.
-bool get_splitk_workspace(hipStream_t stream, size_t ws_bytes, size_t n_counters, float **ws, int **counters);
-
-// Kernel family setting shared by the entry points (see dg_set_kernel_family).
+// Kernel family setting of the calling thread (see dg_set_kernel_family).
 int kernel_family_from_name(const char *name);
 const char *kernel_family_name(int f);
-std::atomic<int> &kernel_family_setting();
+int &kernel_family_setting();
 
 // Chooses a kernel configuration, launches it on `stream`, and describes the
 // choice in `config`.  Returns the HIP error of the launch.

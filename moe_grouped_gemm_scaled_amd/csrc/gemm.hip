@@ -22,8 +22,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <atomic>
-
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -269,13 +267,15 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
     snprintf(buf, sizeof buf, "family=tiled mode=%d tile=%dx%dx128 waves=%dx%d grid=%lld", (int)MODE, BM, BN, WM,
              WN, (long long)grid);
     config = buf;
+    if (p.plan) return hipSuccess;
     hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, MODE>), dim3((unsigned)grid), dim3(64 * WM * WN), 0,
                        stream, k);
     return hipGetLastError();
 }
 
 // Kernel family setting (0 = automatic, 1 skinny, 2 pipe, 3 tiled, 4
-// persist); initialised from DG_KERNEL_FAMILY, changed by dg_set_kernel_family.
+// persist), one per thread: every thread starts from DG_KERNEL_FAMILY (read
+// once per process) and dg_set_kernel_family changes the calling thread's.
 static const char *const kFamilyNames[] = {"auto", "skinny", "pipe", "tiled", "persist"};
 
 int kernel_family_from_name(const char *name) {
@@ -286,12 +286,17 @@ int kernel_family_from_name(const char *name) {
 
 const char *kernel_family_name(int f) { return f >= 0 && f < 5 ? kFamilyNames[f] : "auto"; }
 
-std::atomic<int> &kernel_family_setting() {
-    static std::atomic<int> f([] {
+static int family_from_env() {
+    static const int v = [] {
         const char *e = getenv("DG_KERNEL_FAMILY");
-        const int v = e ? kernel_family_from_name(e) : 0;
-        return v < 0 ? 0 : v;
-    }());
+        const int f = e ? kernel_family_from_name(e) : 0;
+        return f < 0 ? 0 : f;
+    }();
+    return v;
+}
+
+int &kernel_family_setting() {
+    thread_local int f = family_from_env();
     return f;
 }
 
@@ -299,7 +304,7 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
     // MN-major operands (NN, TN, TT layouts): the pipelined family only,
     // whatever the family setting
     if (p.a_mn || p.b_mn) return launch_pipe(p, num_cus, stream, config);
-    const int f = kernel_family_setting().load(std::memory_order_relaxed);
+    const int f = kernel_family_setting();
     if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
     if (f == 2 && pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);
     if (f == 4 && persist_eligible(p)) {

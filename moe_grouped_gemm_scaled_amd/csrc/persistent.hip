@@ -689,8 +689,8 @@ hipError_t launch_persist_t(const GemmProblem &p, int workers, hipStream_t strea
         if (slots > 1) {
             const size_t part = (size_t)BM * BN * sizeof(float);
             if (slots * BM * BN * 4 >= ((int64_t)1 << 31) ||
-                !get_splitk_workspace(stream, part * tiles * slots, (size_t)tiles, &k.ws, &k.counters))
-                return hipErrorNotReady;               // the caller picks another kernel
+                !take_splitk_scratch(p, part * tiles * slots, (size_t)tiles, &k.ws, &k.counters))
+                return hipErrorNotReady;               // no scratch: the caller picks another kernel
         }
     } else if (grid > tiles) {
         grid = tiles;
@@ -702,6 +702,7 @@ hipError_t launch_persist_t(const GemmProblem &p, int workers, hipStream_t strea
              "grid=%lld",
              (int)MODE, BM, BN, WGM, WGN, NST, KS, (int)DEEP, (int)STREAMK, (long long)grid);
     config = buf;
+    if (p.plan) return hipSuccess;
     hipLaunchKernelGGL((persist_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, STREAMK>), dim3((unsigned)grid),
                        dim3(64 * WGM * WGN), 0, stream, k);
     return hipGetLastError();

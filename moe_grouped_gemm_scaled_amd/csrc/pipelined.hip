@@ -794,7 +794,7 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
         const int64_t slots = lo + (hi > 0 ? 1 : 0);
         const size_t per = (size_t)BM * BN * sizeof(float);
         if (slots > 1 && slots * BM * BN * 4 < ((int64_t)1 << 31) &&
-            get_splitk_workspace(stream, per * tiles * slots, (size_t)tiles, &k.ws, &k.counters)) {
+            take_splitk_scratch(p, per * tiles * slots, (size_t)tiles, &k.ws, &k.counters)) {
             k.splits_lo = (int)lo;
             k.split_hi = (int)hi;
             k.slots = (int)slots;
@@ -811,6 +811,7 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
              split && k.split_hi > 0 ? "+" : "", (long long)grid, UE ? " scales=ue8m0" : "",
              AMN ? (BMN ? " layout=tn" : " layout=tt") : (BMN ? " layout=nn" : ""));
     config = buf;
+    if (p.plan) return hipSuccess;
     if constexpr (SPLIT) {
         if (split) {
             hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true, UE, AMN, BMN>),

@@ -16,6 +16,9 @@ Streams: 0 = A, 1 = B, 2 = C, 3 = counts (token counts, masked_m).
 """
 from __future__ import annotations
 
+import concurrent.futures
+import os
+
 import numpy as np
 
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -51,16 +54,32 @@ def uniform(seed: int, stream: int, n: int, start: int = 0) -> np.ndarray:
     return (raw_u64(seed, stream, start, n) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
 
 
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def normal_f32(seed: int, stream: int, shape) -> np.ndarray:
-    """fp32 N(0, 1) array of the given shape (C order), chunked to bound memory."""
+    """fp32 N(0, 1) array of the given shape (C order), in chunks of 2^22
+    values; chunks are independent (counter-based), so large arrays are
+    filled by a few threads at once (numpy releases the GIL in these loops)
+    with the same result."""
     n = int(np.prod(shape, dtype=np.int64))
     out = np.empty(n, dtype=np.float32)
-    for lo in range(0, n, _CHUNK):
+
+    def fill(lo):
         cnt = min(_CHUNK, n - lo)
         u = uniform(seed, stream, 2 * cnt, start=2 * lo)
         u1 = 1.0 - u[0::2]
         u2 = u[1::2]
         out[lo:lo + cnt] = (np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)).astype(np.float32)
+
+    starts = range(0, n, _CHUNK)
+    if n <= 2 * _CHUNK:
+        for lo in starts:
+            fill(lo)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, starts))
     return out.reshape(shape)
 
 

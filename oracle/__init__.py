@@ -54,6 +54,7 @@ def _load():
         "orc_mqa_logits": (None, [P, P, P, P, P, P, I, I, I, I, I, P]),
         "orc_mqa_logits_rows": (None, [P, P, P, P, P, P, I, I, I, I, P, I, P]),
         "orc_num_threads": (I, []),
+        "orc_set_num_threads": (None, [I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -326,3 +327,8 @@ def mqa_logits_rows(q, kv, kv_scale, weights, k_start, k_end, clean_logits, rows
 
 def num_threads():
     return _load().orc_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the oracle's parallel loops from here on (the same results with any count)."""
+    _load().orc_set_num_threads(int(n))

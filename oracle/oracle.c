@@ -511,3 +511,14 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads of the parallel loops from here on (n >= 1); used to time the
+ * oracle on one core beside its all-core time. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -169,6 +169,7 @@ void orc_mqa_logits_rows(const uint8_t *q, const uint8_t *kv, const float *kv_sc
 
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,40 @@ def test_kernel_family_setting(lib):
         lib.dg_set_kernel_family(start.encode())
 
 
+def test_kernel_family_setting_is_per_thread(lib):
+    """A thread's setting changes that thread's kernel choice only."""
+    import threading
+    seen = {}
+
+    def worker():
+        seen["before"] = lib.dg_get_kernel_family().decode()
+        assert lib.dg_set_kernel_family(b"tiled") == 0
+        seen["after"] = lib.dg_get_kernel_family().decode()
+
+    start = lib.dg_get_kernel_family().decode()
+    try:
+        assert lib.dg_set_kernel_family(b"persist") == 0
+        t = threading.Thread(target=worker)
+        t.start()
+        t.join()
+        assert seen["after"] == "tiled"
+        assert seen["before"] != "persist"          # the new thread starts from the environment, not from us
+        assert lib.dg_get_kernel_family().decode() == "persist"
+    finally:
+        lib.dg_set_kernel_family(start.encode())
+
+
+def test_workspace_entry_point_argument_errors(lib):
+    f = lib.dg_fp8_gemm_nt_ws
+    # a, sfa, ld_sfa, b, sfb, c, d, M, N, K, workspace, bytes, stream
+    assert f(NULL, P, 64, P, P, NULL, P, 64, 64, 128, P, 1 << 20, S) == -1
+    assert f(P, P, 64, P, P, NULL, P, 64, 64, 100, P, 1 << 20, S) == -2
+    assert f(P, P, 64, P, P, NULL, P, 64, 64, 128, MIS, 1 << 20, S) == -3     # misaligned workspace
+    assert lib.dg_fp8_gemm_nt_ue8m0_ws(P, P, 64, P, P, NULL, P, 64, 64, 128, MIS, 1 << 20, S) == -3
+    assert lib.dg_get_workspace_size(64, 64, 100) == -2
+    assert lib.dg_get_workspace_size(0, 64, 128) == -2
+
+
 def test_dense_argument_errors(lib):
     f = lib.dg_fp8_gemm_nt
     # a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream

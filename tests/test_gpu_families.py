@@ -118,12 +118,16 @@ def test_contiguous_every_family(family):
 @pytest.mark.parametrize("family", FAMILIES, indirect=True)
 def test_repeated_calls_leave_split_counters_clean(family):
     """Split-K and stream-K reset their per-tile counters; back-to-back calls
-    of different shapes on one stream must all be right."""
+    of different shapes on one stream, all through one caller workspace, must
+    all be right."""
     announce(f"family={family} repeated split calls")
-    for M, N, K in [(64, 700, 4096), (128, 300, 2048), (64, 700, 4096), (40, 1500, 1024)]:
+    shapes = [(64, 700, 4096), (128, 300, 2048), (64, 700, 4096), (40, 1500, 1024)]
+    need = max(dg.get_workspace_size(M, N, K) for M, N, K in shapes)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    for M, N, K in shapes:
         p = dense_problem(M, N, K, seed=M + N + K + 7, with_c=False)
         out = Guarded((M, N))
-        dg.fp8_gemm_nt(dev(p["a"]), dev(p["sfa"]), dev(p["b"]), dev(p["sfb"]), out.t)
+        dg.fp8_gemm_nt(dev(p["a"]), dev(p["sfa"]), dev(p["b"]), dev(p["sfb"]), out.t, workspace=ws)
         torch.cuda.synchronize()
         assert out.guards_intact()
         ref = oracle.gemm_nt(p["a"], p["sfa"], p["b"], p["sfb"], None)

@@ -318,7 +318,7 @@ def test_masked_full_size_sampled():
 
 def test_split_k_on_concurrent_streams():
     """Split-K decode GEMMs issued on three streams at once, repeated: each
-    stream has its own workspace and counters, so concurrent calls must not
+    call brings its own workspace and counters, so concurrent calls must not
     disturb each other (every result to the oracle bar, every time)."""
     shapes = [(64, 2112, 7168), (128, 7168, 2048), (64, 7168, 4096)]
     announce(f"split-K on concurrent streams {shapes}")
