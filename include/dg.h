@@ -57,7 +57,8 @@ typedef enum dg_status {
     DG_ERR_ALIGN = -3,       /* a pointer or leading dimension is misaligned */
     DG_ERR_ARG = -4,         /* any other invalid argument */
     DG_ERR_UNSUPPORTED = -5, /* valid but not supported here (e.g. not a gfx950 device) */
-    DG_ERR_HIP = -6          /* a HIP runtime call failed */
+    DG_ERR_HIP = -6,         /* a HIP runtime call failed */
+    DG_ERR_SCRATCH = -7      /* more scratch needed than dg_fp8_gemm_nt_noalloc holds */
 } dg_status;
 
 /*
@@ -107,6 +108,25 @@ int dg_fp8_gemm_nt_ue8m0_ws(const uint8_t *a, const float *sfa, int ld_sfa,
                             const uint16_t *c, uint16_t *d,
                             int M, int N, int K,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Allocation-free dense GEMM, for callers that cannot allocate device memory
+ * (code under graph capture, serving loops that forbid allocation): the
+ * results of dg_fp8_gemm_nt_ws with a large enough workspace, the split-K
+ * scratch being the library's own device array of 32 MiB per GPU (loaded
+ * with the library's code and held until the process ends; its counters are
+ * cleared on the first call per device).  Allocates and frees nothing.
+ * Every call on a GPU shares that GPU's array: calls that may overlap in time
+ * on one GPU (other streams, concurrently replayed graphs) race, and must use
+ * dg_fp8_gemm_nt_ws with separate workspaces instead.  Same arguments and
+ * errors as dg_fp8_gemm_nt, plus DG_ERR_SCRATCH when the configuration the
+ * call chooses needs more scratch than the array holds (more than 32 MiB of
+ * partials, or more than 16384 split tiles); nothing is launched then.
+ */
+int dg_fp8_gemm_nt_noalloc(const uint8_t *a, const float *sfa, int ld_sfa,
+                           const uint8_t *b, const float *sfb,
+                           const uint16_t *c, uint16_t *d,
+                           int M, int N, int K, void *stream);
 
 /*
  * Workspace bytes for dg_fp8_gemm_nt_ws and dg_fp8_gemm_nt_ue8m0_ws on an

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libdg.so")
 
 DG_OK = 0
 _STATUS = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_ALIGN", -4: "DG_ERR_ARG",
-           -5: "DG_ERR_UNSUPPORTED", -6: "DG_ERR_HIP"}
+           -5: "DG_ERR_UNSUPPORTED", -6: "DG_ERR_HIP", -7: "DG_ERR_SCRATCH"}
 
 EXPORTS = {
     # name: (restype, argtypes)
@@ -35,6 +35,8 @@ EXPORTS = {
                                            ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p,
                                            ct.c_size_t, ct.c_void_p]),
     "dg_get_workspace_size": (ct.c_int64, [ct.c_int, ct.c_int, ct.c_int]),
+    "dg_fp8_gemm_nt_noalloc": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p,
+                                          ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
     "dg_m_grouped_fp8_gemm_nt_contiguous": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                                        ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int,
                                                        ct.c_int, ct.c_int, ct.c_void_p]),
@@ -194,6 +196,21 @@ def fp8_gemm_nt(a, sfa, b, sfb, d, c=None, ue8m0=False, workspace="auto"):
         name = "dg_fp8_gemm_nt_ue8m0_ws" if ue8m0 else "dg_fp8_gemm_nt_ws"
         ws = _ptr(workspace, torch.uint8, "workspace")
         _check(getattr(lib(), name)(*args, ws, int(workspace.numel()), _stream(d)), name)
+    return d
+
+
+def fp8_gemm_nt_noalloc(a, sfa, b, sfb, d, c=None):
+    """D = C + A . B^T through dg_fp8_gemm_nt_noalloc: split-K scratch from the library's own device array,
+    nothing allocated (not even by torch); calls that may overlap on one GPU race.  Arguments as for
+    fp8_gemm_nt."""
+    M, K = a.shape
+    N = b.shape[0]
+    if sfa.dim() != 2 or sfa.shape[0] != K // 128:
+        raise ValueError(f"sfa: shape {tuple(sfa.shape)}, expected [K/128={K // 128}, ld_sfa]")
+    args = (_ptr(a, _FP8, "a", (M, K)), _ptr(sfa, torch.float32, "sfa"), int(sfa.shape[1]),
+            _ptr(b, _FP8, "b", (N, K)), _ptr(sfb, torch.float32, "sfb", (ceil_div(N, 128), K // 128)),
+            _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K, _stream(d))
+    _check(lib().dg_fp8_gemm_nt_noalloc(*args), "dg_fp8_gemm_nt_noalloc")
     return d
 
 

@@ -50,13 +50,16 @@ int current_device(int &dev, int &cus) {
     return DG_OK;
 }
 
-// Scratch bytes the configuration chosen for p needs (0: it does not split K).
-int plan_scratch(const dg::GemmProblem &p, int cus, size_t &need) {
+// Scratch bytes (and arrival counters) the configuration chosen for p needs
+// (0: it does not split K).
+int plan_scratch(const dg::GemmProblem &p, int cus, size_t &need, size_t *counters = nullptr) {
     dg::GemmProblem q = p;
     q.ws = nullptr;
     q.ws_bytes = 0;
     need = 0;
     q.plan = &need;
+    if (counters) *counters = 0;
+    q.plan_counters = counters;
     std::string cfg;
     return dg::launch_gemm(q, cus, nullptr, cfg) == hipSuccess ? DG_OK : DG_ERR_ARG;
 }
@@ -226,6 +229,40 @@ int dg_fp8_gemm_nt_ue8m0_ws(const uint8_t *a, const float *sfa, int ld_sfa, cons
     return gemm_nt_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, workspace, workspace_bytes, stream, true);
 }
 
+// Allocation-free form of dg_fp8_gemm_nt_ws: the split-K scratch is the
+// library's own device array (noalloc.hip).  Nothing is allocated or freed.
+static int gemm_nt_noalloc_impl(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b,
+                                const float *sfb, const uint16_t *c, uint16_t *d, int M, int N, int K,
+                                void *stream, bool ue8m0) {
+    if (!a || !sfa || !b || !sfb || !d) return DG_ERR_NULL;
+    if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
+    if (ld_sfa < M || ld_sfa % 4 != 0) return DG_ERR_ALIGN;
+    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+        (c && !aligned16(c)))
+        return DG_ERR_ALIGN;
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) return st;
+    dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, ue8m0};
+    size_t need = 0, counters = 0;
+    const int ps = plan_scratch(p, cus, need, &counters);
+    if (ps != DG_OK) return ps;
+    if (need > dg::kNoallocScratchBytes || counters > dg::kNoallocMaxCounters) return DG_ERR_SCRATCH;
+    if (need > 0) {
+        void *ptr = nullptr;
+        size_t bytes = 0;
+        if (dg::noalloc_scratch(static_cast<hipStream_t>(stream), &ptr, &bytes) != hipSuccess) return DG_ERR_HIP;
+        p.ws = ptr;
+        p.ws_bytes = bytes;
+    }
+    return run_gemm(p, stream);
+}
+
+int dg_fp8_gemm_nt_noalloc(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
+                           const uint16_t *c, uint16_t *d, int M, int N, int K, void *stream) {
+    return gemm_nt_noalloc_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false);
+}
+
 int64_t dg_get_workspace_size(int M, int N, int K) {
     if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     int dev = 0, cus = 0;
@@ -379,6 +416,8 @@ const char *dg_status_string(int status) {
     case DG_ERR_ARG: return "DG_ERR_ARG: invalid argument";
     case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED: not supported on this device";
     case DG_ERR_HIP: return "DG_ERR_HIP: a HIP runtime call failed";
+    case DG_ERR_SCRATCH:
+        return "DG_ERR_SCRATCH: the problem needs more split-K scratch than the allocation-free entry point holds";
     default: return "unknown dg_status";
     }
 }

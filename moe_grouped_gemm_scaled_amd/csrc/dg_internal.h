@@ -59,8 +59,9 @@ struct GemmProblem {
     size_t ws_bytes = 0;
     // planning: when set, the launchers take the configuration they would
     // take with a large enough scratch, store the scratch bytes it needs
-    // here, and launch nothing
+    // here (and its arrival counters in *plan_counters), and launch nothing
     size_t *plan = nullptr;
+    size_t *plan_counters = nullptr;
 };
 
 // Bytes of split-K scratch for `partial_bytes` of fp32 partials and
@@ -82,6 +83,7 @@ inline bool take_splitk_scratch(const GemmProblem &p, size_t partial_bytes, size
     *counters = nullptr;
     if (p.plan) {
         if (need > *p.plan) *p.plan = need;
+        if (p.plan_counters && n_counters > *p.plan_counters) *p.plan_counters = n_counters;
         return true;
     }
     if (!p.ws || p.ws_bytes < need) return false;
@@ -105,6 +107,16 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
 // does not take the problem; the caller then picks another family.
 bool persist_eligible(const GemmProblem &p);
 hipError_t launch_persist(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
+
+// The allocation-free entry point's scratch: a device array of
+// kNoallocScratchBytes per GPU (noalloc.hip).  Its address on the current
+// device (looked up, and its counters cleared, on the first call per device).
+// Its counter region is cleared for up to kNoallocMaxCounters tiles; problems
+// with more split tiles than that, or more scratch than the array holds, are
+// rejected by the entry point.
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+constexpr size_t kNoallocMaxCounters = 16384;
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr, size_t *bytes);
 
 // Kernel family setting of the calling thread (see dg_set_kernel_family).
 int kernel_family_from_name(const char *name);

@@ -48,7 +48,7 @@ def test_utilities(lib):
     assert [lib.dg_get_sf_aligned_size(x) for x in (1, 4, 5, 128, 130)] == [4, 4, 8, 128, 132]
     assert lib.dg_set_num_cus(-1) == -4
     assert lib.dg_set_num_cus(0) == 0
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert lib.dg_status_string(s).decode().startswith(("DG_OK", "DG_ERR"))
 
 
@@ -97,6 +97,16 @@ def test_workspace_entry_point_argument_errors(lib):
     assert lib.dg_fp8_gemm_nt_ue8m0_ws(P, P, 64, P, P, NULL, P, 64, 64, 128, MIS, 1 << 20, S) == -3
     assert lib.dg_get_workspace_size(64, 64, 100) == -2
     assert lib.dg_get_workspace_size(0, 64, 128) == -2
+
+
+def test_noalloc_entry_point_argument_errors(lib):
+    f = lib.dg_fp8_gemm_nt_noalloc
+    # a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream
+    assert f(NULL, P, 64, P, P, NULL, P, 64, 64, 128, S) == -1
+    assert f(P, P, 64, P, P, NULL, P, 64, 64, 100, S) == -2
+    assert f(P, P, 60, P, P, NULL, P, 64, 64, 128, S) == -3
+    assert f(MIS, P, 64, P, P, NULL, P, 64, 64, 128, S) == -3
+    assert lib.dg_status_string(-7).decode().startswith("DG_ERR_SCRATCH")
 
 
 def test_dense_argument_errors(lib):
