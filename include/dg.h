@@ -87,11 +87,12 @@ int dg_fp8_gemm_nt(const uint8_t *a, const float *sfa, int ld_sfa,
  *   workspace_bytes  its size; at least dg_get_workspace_size(M, N, K) for
  *                    the configuration the call chooses (DG_ERR_ARG
  *                    otherwise, before anything is launched).
- * Layout: the workspace starts with one int32 arrival counter per output
- * tile, which must be ZERO when a call starts; every call that completes
- * leaves them zero again, so memory zeroed once (hipMemset, torch.zeros)
- * serves any number of calls in stream order, eager or captured in a graph.
- * The rest holds the fp32 partial tiles of the K splits.  The caller owns
+ * Layout: the workspace starts with a fixed 16 KiB region of int32 arrival
+ * counters (one per output tile of a split call), which must be ZERO when a
+ * call starts; every call that completes leaves them zero again, so memory
+ * zeroed once (hipMemset, torch.zeros) serves any number of calls of any
+ * shapes in stream order, eager or captured in a graph.  The rest holds the
+ * fp32 partial tiles of the K splits.  The caller owns
  * the workspace; it must stay allocated until the call's work completes, and
  * two calls that may run at the same time (other streams, concurrently
  * replayed graphs) need two workspaces.  The partials of the splits are
@@ -120,8 +121,8 @@ int dg_fp8_gemm_nt_ue8m0_ws(const uint8_t *a, const float *sfa, int ld_sfa,
  * on one GPU (other streams, concurrently replayed graphs) race, and must use
  * dg_fp8_gemm_nt_ws with separate workspaces instead.  Same arguments and
  * errors as dg_fp8_gemm_nt, plus DG_ERR_SCRATCH when the configuration the
- * call chooses needs more scratch than the array holds (more than 32 MiB of
- * partials, or more than 16384 split tiles); nothing is launched then.
+ * call chooses needs more scratch than the array holds (more than 32 MiB
+ * with its 16 KiB of counters); nothing is launched then.
  */
 int dg_fp8_gemm_nt_noalloc(const uint8_t *a, const float *sfa, int ld_sfa,
                            const uint8_t *b, const float *sfb,

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "decode.hip", "pipelined.hip", "persistent.hip", "mqa.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "decode.hip", "pipelined.hip", "persistent.hip", "mqa.hip", "noalloc.hip", "stream.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 from the compiler.

@@ -50,16 +50,13 @@ int current_device(int &dev, int &cus) {
     return DG_OK;
 }
 
-// Scratch bytes (and arrival counters) the configuration chosen for p needs
-// (0: it does not split K).
-int plan_scratch(const dg::GemmProblem &p, int cus, size_t &need, size_t *counters = nullptr) {
+// Scratch bytes the configuration chosen for p needs (0: it does not split K).
+int plan_scratch(const dg::GemmProblem &p, int cus, size_t &need) {
     dg::GemmProblem q = p;
     q.ws = nullptr;
     q.ws_bytes = 0;
     need = 0;
     q.plan = &need;
-    if (counters) *counters = 0;
-    q.plan_counters = counters;
     std::string cfg;
     return dg::launch_gemm(q, cus, nullptr, cfg) == hipSuccess ? DG_OK : DG_ERR_ARG;
 }
@@ -244,10 +241,10 @@ static int gemm_nt_noalloc_impl(const uint8_t *a, const float *sfa, int ld_sfa, 
     const int st = current_device(dev, cus);
     if (st != DG_OK) return st;
     dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, ue8m0};
-    size_t need = 0, counters = 0;
-    const int ps = plan_scratch(p, cus, need, &counters);
+    size_t need = 0;
+    const int ps = plan_scratch(p, cus, need);
     if (ps != DG_OK) return ps;
-    if (need > dg::kNoallocScratchBytes || counters > dg::kNoallocMaxCounters) return DG_ERR_SCRATCH;
+    if (need > dg::kNoallocScratchBytes) return DG_ERR_SCRATCH;
     if (need > 0) {
         void *ptr = nullptr;
         size_t bytes = 0;

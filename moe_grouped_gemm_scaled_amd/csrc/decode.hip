@@ -18,6 +18,10 @@
 //    LDS banks).  Every step issues the same loads, so the compiler's
 //    in-order memory-counter waits stay exact; there is no separate
 //    prologue (the ring starts zeroed and the first PD steps only fill it);
+//  - each workgroup walks its K blocks from a start given by a hash of its
+//    id, wrapping around, so that workgroups stream different K offsets at
+//    the same time (measured on MI355X at N = 24576, K = 1536: 11.8 -> 11.4 us
+//    at M = 64, 15.5 -> 14.6 us at M = 128);
 //  - optional split-K: S workgroups cover disjoint K ranges of one tile.
 //    Each writes its fp32 partial with device-coherent (sc1) 16-byte
 //    stores, waits for them, and bumps a per-tile counter; the last to
@@ -232,6 +236,12 @@ skinny_kernel(SkinnyParams p) {
     // and blocks outside [kb0 + t*KS, kb1) are multiplied with a zero scale.
     const int nsteps = (kb1 - kb0 + KS - 1) / KS;
     const int last_kb = kb1 - KS >= 0 ? kb1 - KS : 0;
+    // with one K block per step the blocks may be walked in any order: from
+    // a hashed start, wrapping around (the data of logical block x is
+    // physical block kb0 + rotated(x))
+    const int nb_all = kb1 - kb0;
+    const int rot = KS == 1 ? k_rotation(blockIdx.x, nb_all) : 0;
+    auto rotated = [&](int x) __attribute__((always_inline)) { return x + rot < nb_all ? x + rot : x + rot - nb_all; };
     const int ngroups = (nsteps + PD - 1) / PD;
     for (int gi = -1; gi < ngroups; ++gi) {
         static_for<PD>([&](auto uc) __attribute__((always_inline)) {
@@ -253,7 +263,7 @@ skinny_kernel(SkinnyParams p) {
                 if (gs_store[i]) *reinterpret_cast<float *>(st + gs_off[i]) = rs[u][i];
             });
             const int kn = min(kb0 + (t + PD) * KS, last_kb);
-            issue(kn, uc);
+            issue(kb0 + rotated(kn - kb0), uc);
             __syncthreads();
 
             // K blocks held by the stage start at kdata; the step owns [kstart, kstart + KS) ∩ [kb0, kb1).

@@ -53,23 +53,26 @@ struct GemmProblem {
     const float *c32 = nullptr;
     float *d32 = nullptr;
     // split-K scratch brought in by the caller (dense calls only; NULL: the
-    // launchers run without split-K).  Layout: the int32 arrival counters
-    // first (the region rounded up to 256 bytes), then the fp32 partials.
+    // launchers run without split-K).  Layout: a fixed region of
+    // kSplitCounters int32 arrival counters, then the fp32 partials.
     void *ws = nullptr;
     size_t ws_bytes = 0;
     // planning: when set, the launchers take the configuration they would
     // take with a large enough scratch, store the scratch bytes it needs
-    // here (and its arrival counters in *plan_counters), and launch nothing
+    // here, and launch nothing
     size_t *plan = nullptr;
-    size_t *plan_counters = nullptr;
 };
 
-// Bytes of split-K scratch for `partial_bytes` of fp32 partials and
-// `n_counters` arrival counters (laid out as described above).
-constexpr size_t splitk_counter_bytes(size_t n_counters) { return (n_counters * 4 + 255) / 256 * 256; }
-constexpr size_t splitk_scratch_bytes(size_t partial_bytes, size_t n_counters) {
-    return splitk_counter_bytes(n_counters) + partial_bytes;
-}
+// The counter region has the same size whatever the problem, so that one
+// scratch can serve calls of different shapes in turn: each call's partials
+// start past every call's counters, which completed calls leave at zero.  A
+// split problem has fewer tiles than workgroups (at most a few per CU), far
+// below this; a configuration that would need more declines to split.
+constexpr size_t kSplitCounters = 4096;
+constexpr size_t kSplitCounterBytes = kSplitCounters * 4;
+
+// Bytes of split-K scratch for `partial_bytes` of fp32 partials.
+constexpr size_t splitk_scratch_bytes(size_t partial_bytes) { return kSplitCounterBytes + partial_bytes; }
 
 // The split-K scratch of a launch.  Planning: records the need in *p.plan and
 // grants (the launcher then returns before launching).  Otherwise grants the
@@ -78,17 +81,17 @@ constexpr size_t splitk_scratch_bytes(size_t partial_bytes, size_t n_counters) {
 // none or it is too small.
 inline bool take_splitk_scratch(const GemmProblem &p, size_t partial_bytes, size_t n_counters, float **ws,
                                 int **counters) {
-    const size_t need = splitk_scratch_bytes(partial_bytes, n_counters);
+    const size_t need = splitk_scratch_bytes(partial_bytes);
     *ws = nullptr;
     *counters = nullptr;
+    if (n_counters > kSplitCounters) return false;
     if (p.plan) {
         if (need > *p.plan) *p.plan = need;
-        if (p.plan_counters && n_counters > *p.plan_counters) *p.plan_counters = n_counters;
         return true;
     }
     if (!p.ws || p.ws_bytes < need) return false;
     *counters = static_cast<int *>(p.ws);
-    *ws = reinterpret_cast<float *>(static_cast<char *>(p.ws) + splitk_counter_bytes(n_counters));
+    *ws = reinterpret_cast<float *>(static_cast<char *>(p.ws) + kSplitCounterBytes);
     return true;
 }
 
@@ -96,6 +99,11 @@ inline bool take_splitk_scratch(const GemmProblem &p, size_t partial_bytes, size
 // and every operand below 2 GB (32-bit buffer offsets).
 bool skinny_eligible(const GemmProblem &p);
 hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
+
+// Streaming family for decode shapes (dense, M <= 128): B loaded straight
+// into a per-wave register ring, A through an LDS ring, optional split-K.
+bool stream_eligible(const GemmProblem &p);
+hipError_t launch_stream(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
 
 // Pipelined family (multi-stage LDS-DMA pipeline, optional split-K): every
 // mode and shape; needs every operand below 2 GB (32-bit buffer offsets).
@@ -110,12 +118,10 @@ hipError_t launch_persist(const GemmProblem &p, int num_cus, hipStream_t stream,
 
 // The allocation-free entry point's scratch: a device array of
 // kNoallocScratchBytes per GPU (noalloc.hip).  Its address on the current
-// device (looked up, and its counters cleared, on the first call per device).
-// Its counter region is cleared for up to kNoallocMaxCounters tiles; problems
-// with more split tiles than that, or more scratch than the array holds, are
+// device (looked up, and its counter region cleared, on the first call per
+// device).  Problems whose split needs more scratch than the array holds are
 // rejected by the entry point.
 constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
-constexpr size_t kNoallocMaxCounters = 16384;
 hipError_t noalloc_scratch(hipStream_t stream, void **ptr, size_t *bytes);
 
 // Kernel family setting of the calling thread (see dg_set_kernel_family).

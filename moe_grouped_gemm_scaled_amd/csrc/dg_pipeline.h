@@ -46,6 +46,12 @@ __device__ __forceinline__ void dma_step(uint8_t *stg, __amdgpu_buffer_rsrc_t rA
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, DG_LDS(stg + lds_s), 16, v_s, s_off, 0, 0);
 }
 
+// One 16-byte-per-lane buffer load into LDS (1 KB per wave at `dst`).
+// Device-only for the same reason as dma_step.
+__device__ __forceinline__ void dma_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *dst, int voffset, int soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, DG_LDS(dst), 16, voffset, soffset, 0, 0);
+}
+
 // MFMA fragment of an operand stored MN-major in LDS: rows are K (PITCH
 // bytes each, 16-byte columns XOR-swizzled by (row & 7)), columns are M (or
 // N).  gfx950's ds_read_b64_tr_b8 gathers, in each group of 16 lanes, byte

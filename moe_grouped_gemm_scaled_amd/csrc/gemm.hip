@@ -274,17 +274,19 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
 }
 
 // Kernel family setting (0 = automatic, 1 skinny, 2 pipe, 3 tiled, 4
-// persist), one per thread: every thread starts from DG_KERNEL_FAMILY (read
-// once per process) and dg_set_kernel_family changes the calling thread's.
-static const char *const kFamilyNames[] = {"auto", "skinny", "pipe", "tiled", "persist"};
+// persist, 5 stream), one per thread: every thread starts from
+// DG_KERNEL_FAMILY (read once per process) and dg_set_kernel_family changes
+// the calling thread's.
+static const char *const kFamilyNames[] = {"auto", "skinny", "pipe", "tiled", "persist", "stream"};
+constexpr int kFamilies = 6;
 
 int kernel_family_from_name(const char *name) {
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < kFamilies; ++i)
         if (!strcmp(name, kFamilyNames[i])) return i;
     return -1;
 }
 
-const char *kernel_family_name(int f) { return f >= 0 && f < 5 ? kFamilyNames[f] : "auto"; }
+const char *kernel_family_name(int f) { return f >= 0 && f < kFamilies ? kFamilyNames[f] : "auto"; }
 
 static int family_from_env() {
     static const int v = [] {
@@ -306,6 +308,7 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
     if (p.a_mn || p.b_mn) return launch_pipe(p, num_cus, stream, config);
     const int f = kernel_family_setting();
     if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
+    if (f == 5 && stream_eligible(p)) return launch_stream(p, num_cus, stream, config);
     if (f == 2 && pipe_eligible(p)) return launch_pipe(p, num_cus, stream, config);
     if (f == 4 && persist_eligible(p)) {
         const hipError_t e = launch_persist(p, num_cus, stream, config);
@@ -325,6 +328,11 @@ hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, st
     const int cus = num_cus > 0 ? num_cus : 256;
     if (p.mode == Mode::Dense && p.rows_a <= 128 && skinny_eligible(p) && (int64_t)(p.N + 127) / 128 * 10 >= (int64_t)cus * 7)
         return launch_skinny(p, num_cus, stream, config);
+    // Other decode-shaped dense problems: the streaming family (32-column
+    // tiles for narrow N, 128-column tiles otherwise, split-K; measured for
+    // M in {64, 128}, N = 2112, K = 7168 and N = 7168, K = 16384).  With
+    // power-of-two scales the pipelined family applies them in the MFMA.
+    if (p.mode == Mode::Dense && !p.ue8m0 && stream_eligible(p)) return launch_stream(p, num_cus, stream, config);
     // Masked layout: the persistent family deals only the row tiles with valid
     // rows to the workgroups (measured on MI355X: 16 groups x 256 rows,
     // N = 7168, K = 2048).

@@ -49,8 +49,7 @@ hipError_t noalloc_scratch(hipStream_t stream, void **ptr, size_t *bytes) {
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
             r = hipStreamIsCapturing(stream, &cs);
             if (r == hipSuccess && cs == hipStreamCaptureStatusNone) {
-                // the counter region of the largest tile count any launcher uses
-                const size_t words = splitk_counter_bytes(kNoallocMaxCounters) / 4;
+                const size_t words = kSplitCounterBytes / 4;
                 hipLaunchKernelGGL(clear_words, dim3(16), dim3(256), 0, stream, static_cast<uint32_t *>(p), words);
                 r = hipGetLastError();
             }

@@ -55,29 +55,43 @@ __device__ __forceinline__ float block_scale(float amax) {
     return __uint_as_float((u & 0x7fffffu) ? (u & 0x7f800000u) + 0x00800000u : u);
 }
 
-// 1x128: a half-wave (32 lanes x float4) per 128-element block; consecutive
-// half-waves take consecutive blocks of a row, so loads and stores coalesce.
-template <bool UE8M0>
+// 1x128: a half-wave (32 lanes x float4) per 128-element block.  A
+// workgroup of 8 half-waves takes 8 consecutive rows (of all groups, flat)
+// and U consecutive K blocks of each: every half-wave issues the loads of
+// its U blocks (one contiguous run of U*512 bytes) before any arithmetic, so
+// U*16 bytes per lane are in flight, and for each K block the 8 scales of the
+// workgroup land in 32 consecutive bytes of the transposed layout.  x is read
+// once: nontemporal loads keep it out of the caches that the codes (read
+// next by the GEMM) live in.
+template <bool UE8M0, int U>
 __global__ void __launch_bounds__(256)
 quant_1x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ sf,
-                   int rows, int nkb, int ld_sf, int64_t nblocks) {
-    const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+                   int rows, int nkb, int ld_sf, int64_t rows_total, int kb_tiles) {
+    const int64_t row_all = (int64_t)(blockIdx.x / kb_tiles) * 8 + (threadIdx.x >> 5);
+    const int kb0 = (int)(blockIdx.x % kb_tiles) * U;
     const int l = threadIdx.x & 31;
-    if (blk >= nblocks) return;
-    const float4 v = reinterpret_cast<const float4 *>(x + blk * kKBlock)[l];
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    if (row_all >= rows_total) return;
+    const float *xr = x + row_all * nkb * kKBlock;
+    v4f v[U];
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
-    const float s = block_scale<UE8M0>(amax);
-    const uint32_t packed = e4m3_encode(v.x / s) | (e4m3_encode(v.y / s) << 8) |
-                            (e4m3_encode(v.z / s) << 16) | (e4m3_encode(v.w / s) << 24);
-    reinterpret_cast<uint32_t *>(q + blk * kKBlock)[l] = packed;
-    if (l == 0) {
-        const int64_t row_all = blk / nkb;                 // g * rows + r
-        const int kb = (int)(blk - row_all * nkb);
-        const int64_t g = row_all / rows;
-        const int r = (int)(row_all - g * rows);
-        sf[(g * nkb + kb) * (int64_t)ld_sf + r] = s;
+    for (int u = 0; u < U; ++u) {
+        if (kb0 + u < nkb)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + (int64_t)(kb0 + u) * kKBlock) + l);
+    }
+    const int64_t g = row_all / rows;
+    const int r = (int)(row_all - g * rows);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int kb = kb0 + u;
+        if (kb >= nkb) break;
+        float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+        const float s = block_scale<UE8M0>(amax);
+        const uint32_t packed = e4m3_encode(v[u].x / s) | (e4m3_encode(v[u].y / s) << 8) |
+                                (e4m3_encode(v[u].z / s) << 16) | (e4m3_encode(v[u].w / s) << 24);
+        reinterpret_cast<uint32_t *>(q + (row_all * nkb + kb) * kKBlock)[l] = packed;
+        if (l == 0) sf[(g * nkb + kb) * (int64_t)ld_sf + r] = s;
     }
 }
 
@@ -125,19 +139,33 @@ quant_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float
     if (t == 0) sf[(g * nrb + rb) * (int64_t)nkb + kb] = s;
 }
 
+template <int U>
+static hipError_t launch_quant_1x128_u(const float *x, int groups, int rows, int nkb, uint8_t *q, float *sf,
+                                       int ld_sf, hipStream_t stream, bool ue8m0) {
+    const int64_t rows_total = (int64_t)groups * rows;
+    const int kb_tiles = (nkb + U - 1) / U;
+    const int64_t grid = (rows_total + 7) / 8 * kb_tiles;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (ue8m0)
+        hipLaunchKernelGGL((quant_1x128_kernel<true, U>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           x, q, sf, rows, nkb, ld_sf, rows_total, kb_tiles);
+    else
+        hipLaunchKernelGGL((quant_1x128_kernel<false, U>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           x, q, sf, rows, nkb, ld_sf, rows_total, kb_tiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
                               int ld_sf, hipStream_t stream, bool ue8m0) {
     const int nkb = K / kKBlock;
-    const int64_t nblocks = (int64_t)groups * rows * nkb;
-    const int64_t grid = (nblocks + 7) / 8;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    if (ue8m0)
-        hipLaunchKernelGGL(quant_1x128_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
-                           x, q, sf, rows, nkb, ld_sf, nblocks);
-    else
-        hipLaunchKernelGGL(quant_1x128_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
-                           x, q, sf, rows, nkb, ld_sf, nblocks);
-    return hipGetLastError();
+    // four blocks per half-wave when that still leaves a few workgroups per
+    // CU; fewer for small (decode) inputs, so that more CUs take a share
+    const int64_t row_groups = ((int64_t)groups * rows + 7) / 8;
+    if (row_groups * ((nkb + 3) / 4) >= 2048)
+        return launch_quant_1x128_u<4>(x, groups, rows, nkb, q, sf, ld_sf, stream, ue8m0);
+    if (row_groups * ((nkb + 1) / 2) >= 1024)
+        return launch_quant_1x128_u<2>(x, groups, rows, nkb, q, sf, ld_sf, stream, ue8m0);
+    return launch_quant_1x128_u<1>(x, groups, rows, nkb, q, sf, ld_sf, stream, ue8m0);
 }
 
 hipError_t launch_quant_128x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,

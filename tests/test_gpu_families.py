@@ -19,6 +19,7 @@ from helpers import SENTINEL, Guarded, check_close, contiguous_problem, dense_pr
 pytestmark = pytest.mark.gpu
 
 FAMILIES = ["pipe", "persist", "skinny", "tiled"]
+DENSE_FAMILIES = FAMILIES + ["stream"]          # the streaming family takes dense problems only
 
 
 def announce(msg):
@@ -53,7 +54,7 @@ DENSE = [(64, 2112, 2048, False), (128, 700, 1536, True), (33, 1000, 384, False)
          (300, 520, 768, True), (520, 300, 2048, False)]
 
 
-@pytest.mark.parametrize("family", FAMILIES, indirect=True)
+@pytest.mark.parametrize("family", DENSE_FAMILIES, indirect=True)
 @pytest.mark.parametrize("M,N,K,with_c", DENSE)
 def test_dense_every_family(family, M, N, K, with_c):
     announce(f"family={family} dense M={M} N={N} K={K} C={with_c}")
@@ -67,7 +68,7 @@ def test_dense_every_family(family, M, N, K, with_c):
     ref = oracle.gemm_nt(p["a"], p["sfa"], p["b"], p["sfb"], p["c"])
     check_close(out.bits(), ref, f"{family} dense {M}x{N}x{K} ({cfg})")
     # the forced family ran wherever it takes the problem
-    takes = {"pipe": True, "tiled": True, "skinny": M <= 128,
+    takes = {"pipe": True, "tiled": True, "skinny": M <= 128, "stream": M <= 128,
              "persist": M > 128 or (K // 128) % 2 == 0}[family]
     if takes:
         assert _family_of(cfg) == family, cfg
@@ -115,7 +116,7 @@ def test_contiguous_every_family(family):
     assert _family_of(cfg) == family, cfg
 
 
-@pytest.mark.parametrize("family", FAMILIES, indirect=True)
+@pytest.mark.parametrize("family", DENSE_FAMILIES, indirect=True)
 def test_repeated_calls_leave_split_counters_clean(family):
     """Split-K and stream-K reset their per-tile counters; back-to-back calls
     of different shapes on one stream, all through one caller workspace, must
