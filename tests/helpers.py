@@ -114,3 +114,26 @@ def sample_indices(n, count, seed, stream=9):
         return np.arange(n, dtype=np.int32)
     pick = synth.randint(seed, stream, count, 0, n - 1)
     return np.unique(np.concatenate([pick, [0, n - 1]])).astype(np.int32)
+
+
+def stratified_indices(n, seed, stream=20, within=None):
+    """One index in every aligned block of 16 of [0, n) (the last block may be
+    partial), its position in the block cycling over all 16 values from a
+    seeded start, plus n - 1.  A mesh of such rows and columns compares every
+    output tile of any width that is a multiple of 16, and every
+    (row mod 16, column mod 16) position, i.e. every lane and register of the
+    16x16 matrix-instruction layout.  `within`: only indices in this sorted
+    array (blocks without any are skipped)."""
+    start = int(synth.randint(seed, stream, 1, 0, 15)[0])
+    out = []
+    for b in range((n + 15) // 16):
+        lo, hi = 16 * b, min(16 * b + 16, n)
+        cand = np.arange(lo, hi) if within is None else within[(within >= lo) & (within < hi)]
+        if cand.size == 0:
+            continue
+        want = lo + (start + 7 * b) % 16
+        out.append(int(cand[np.argmin(np.abs(cand - want))]))
+    last = n - 1 if within is None else (int(within[-1]) if within.size else None)
+    if last is not None:
+        out.append(last)
+    return np.unique(np.array(out, dtype=np.int32))

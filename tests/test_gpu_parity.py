@@ -19,7 +19,7 @@ from moe_grouped_gemm_scaled_amd import binding as dg
 from moe_grouped_gemm_scaled_amd import synth
 
 from helpers import (SENTINEL, Guarded, check_close, contiguous_problem, dense_problem, dev, dev_bf16,
-                     masked_problem, sample_indices)
+                     masked_problem, sample_indices, stratified_indices)
 
 pytestmark = pytest.mark.gpu
 
@@ -250,8 +250,9 @@ def test_dense_full_size_sampled(cfg):
     announce(f"dense full size {cfg['name']}")
     p = dense_problem(M, N, K, cfg["seed"], cfg["with_c"])
     got = run_dense(p)
-    ms = sample_indices(M, 160, cfg["seed"], stream=10)
-    ns = sample_indices(N, 160, cfg["seed"], stream=11)
+    # stratified: every 16-row and 16-column block, every position in it
+    ms = stratified_indices(M, cfg["seed"], stream=10) if M > 128 else np.arange(M, dtype=np.int32)
+    ns = stratified_indices(N, cfg["seed"], stream=11)
     ns = np.unique(np.concatenate([ns, np.arange(max(0, N - 70), N)])).astype(np.int32)   # N tail
     mm, nn = np.meshgrid(ms, ns, indexing="ij")
     ref = oracle.gemm_nt_at(p["a"], p["sfa"], p["b"], p["sfb"], p["c"], mm.reshape(-1), nn.reshape(-1))
@@ -277,9 +278,12 @@ def test_contiguous_full_size_sampled():
     for g in range(cfg["G"]):
         r = np.nonzero(m_idx == g)[0]
         rows += [r[0], r[-1], r[r.size // 2]]
-    rows = np.unique(np.concatenate([np.array(rows), sample_indices(p["M_total"], 48, cfg["seed"])]))
-    rows = rows[m_idx[rows] >= 0].astype(np.int32)
-    ns = sample_indices(cfg["N"], 96, cfg["seed"], stream=12)
+    # stratified over the valid rows (every 16-row block of every expert) and
+    # over the columns (every 16-column block, every position)
+    valid_rows = np.nonzero(m_idx >= 0)[0].astype(np.int32)
+    rows = np.unique(np.concatenate([np.array(rows, dtype=np.int32),
+                                     stratified_indices(p["M_total"], cfg["seed"], stream=14, within=valid_rows)]))
+    ns = stratified_indices(cfg["N"], cfg["seed"], stream=12)
     mm, nn = np.meshgrid(rows, ns, indexing="ij")
     ref = oracle.m_grouped_contiguous_at(p["a"], p["sfa"], p["b"], p["sfb"], None, m_idx,
                                          mm.reshape(-1), nn.reshape(-1))
@@ -299,14 +303,16 @@ def test_masked_full_size_sampled():
     assert out.guards_intact()
     got = out.bits()
     gs, ms, ns = [], [], []
-    col = sample_indices(N, 48, cfg["seed"], stream=13)
+    col = stratified_indices(N, cfg["seed"], stream=13)
     for g in range(G):
         mmg = int(mm_counts[g])
         assert np.all(got[g, mmg:] == SENTINEL), f"group {g}: masked rows written"
         if mmg == 0:
             continue
         assert not np.any((got[g, :mmg] & 0x7F80) == 0x7F80)
-        r = np.unique(np.array([0, mmg - 1, mmg // 2, (mmg * 3) // 4]))
+        # every 16-row block of the valid rows, every position in it
+        r = np.unique(np.concatenate([np.array([0, mmg - 1, mmg // 2]),
+                                      stratified_indices(mmg, cfg["seed"] + g, stream=15)]))
         for rr in r:
             gs += [g] * col.size
             ms += [rr] * col.size
