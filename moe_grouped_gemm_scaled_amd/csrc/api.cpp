@@ -83,6 +83,39 @@ int check_k(int K) { return (K < 128 || K % 128 != 0) ? DG_ERR_SHAPE : DG_OK; }
 
 }  // namespace
 
+namespace dg {
+
+// Kernel family setting (0 = automatic, 1 skinny, 2 pipe, 3 tiled, 4
+// persist, 5 stream), one per thread: every thread starts from
+// DG_KERNEL_FAMILY (read once per process) and dg_set_kernel_family changes
+// the calling thread's.
+static const char *const kFamilyNames[] = {"auto", "skinny", "pipe", "tiled", "persist", "stream"};
+constexpr int kFamilies = 6;
+
+int kernel_family_from_name(const char *name) {
+    for (int i = 0; i < kFamilies; ++i)
+        if (!strcmp(name, kFamilyNames[i])) return i;
+    return -1;
+}
+
+const char *kernel_family_name(int f) { return f >= 0 && f < kFamilies ? kFamilyNames[f] : "auto"; }
+
+static int family_from_env() {
+    static const int v = [] {
+        const char *e = getenv("DG_KERNEL_FAMILY");
+        const int f = e ? kernel_family_from_name(e) : 0;
+        return f < 0 ? 0 : f;
+    }();
+    return v;
+}
+
+int &kernel_family_setting() {
+    thread_local int f = family_from_env();
+    return f;
+}
+
+}  // namespace dg
+
 extern "C" {
 
 static int gemm_nt_impl(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,

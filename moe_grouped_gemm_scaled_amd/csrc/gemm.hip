@@ -273,35 +273,6 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
     return hipGetLastError();
 }
 
-// Kernel family setting (0 = automatic, 1 skinny, 2 pipe, 3 tiled, 4
-// persist, 5 stream), one per thread: every thread starts from
-// DG_KERNEL_FAMILY (read once per process) and dg_set_kernel_family changes
-// the calling thread's.
-static const char *const kFamilyNames[] = {"auto", "skinny", "pipe", "tiled", "persist", "stream"};
-constexpr int kFamilies = 6;
-
-int kernel_family_from_name(const char *name) {
-    for (int i = 0; i < kFamilies; ++i)
-        if (!strcmp(name, kFamilyNames[i])) return i;
-    return -1;
-}
-
-const char *kernel_family_name(int f) { return f >= 0 && f < kFamilies ? kFamilyNames[f] : "auto"; }
-
-static int family_from_env() {
-    static const int v = [] {
-        const char *e = getenv("DG_KERNEL_FAMILY");
-        const int f = e ? kernel_family_from_name(e) : 0;
-        return f < 0 ? 0 : f;
-    }();
-    return v;
-}
-
-int &kernel_family_setting() {
-    thread_local int f = family_from_env();
-    return f;
-}
-
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     // MN-major operands (NN, TN, TT layouts): the pipelined family only,
     // whatever the family setting
