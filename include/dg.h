@@ -299,6 +299,64 @@ int dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(const uint8_t *a, const float *sfa
                                               int M, int N, int K, int G, void *stream);
 
 /*
+ * Packed UE8M0 scales.  The DeepGEMM README summary ("GEMM interface and
+ * layout constraints") states that the SM100 kernels take their scaling
+ * factors as UE8M0 exponents packed four to a 32-bit integer.  The pages do
+ * not fix the packing order; here the four share one row (A) or 128-column
+ * block (B) and four consecutive K blocks: with nkw = ceil(K/512), byte j
+ * (bits 8j .. 8j+7) of word q holds the biased exponent of K block 4q + j
+ * (the fp32 exponent field of the power-of-two scale 2^(e-127)); bytes past
+ * the last K block are ignored.
+ *
+ *   sfa   uint32 [nkw][ld_sfa]           (dense; ld_sfa >= M, multiple of 4)
+ *         uint32 [nkw][M_total]          (contiguous)
+ *         uint32 [G][nkw][ceil4(M_cap)]  (masked)
+ *   sfb   uint32 [ceil(N/128)][nkw]      (dense)
+ *         uint32 [G][ceil(N/128)][nkw]   (grouped)
+ *
+ * Every other argument, the result (bit-identical to the matching *_ue8m0
+ * entry point on the scales the words encode) and the errors are as for
+ * dg_fp8_gemm_nt_ws, dg_m_grouped_fp8_gemm_nt_contiguous and
+ * dg_m_grouped_fp8_gemm_nt_masked, plus DG_ERR_SHAPE when K times M (M_total,
+ * M_cap) or K times N reaches 2^31.  The byte 0 (2^-127) is not a valid
+ * scale, as a scale that is not a normal power of two is not for the
+ * *_ue8m0 forms.
+ */
+int dg_fp8_gemm_nt_ue8m0_packed(const uint8_t *a, const uint32_t *sfa, int ld_sfa,
+                                const uint8_t *b, const uint32_t *sfb,
+                                const uint16_t *c, uint16_t *d,
+                                int M, int N, int K,
+                                void *workspace, size_t workspace_bytes, void *stream);
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed(const uint8_t *a, const uint32_t *sfa,
+                                                     const uint8_t *b, const uint32_t *sfb,
+                                                     const uint16_t *c, uint16_t *d,
+                                                     const int32_t *m_indices,
+                                                     int M_total, int N, int K, int G,
+                                                     void *stream);
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed(const uint8_t *a, const uint32_t *sfa,
+                                                 const uint8_t *b, const uint32_t *sfb,
+                                                 const uint16_t *c, uint16_t *d,
+                                                 const int32_t *masked_m,
+                                                 int G, int M_cap, int N, int K,
+                                                 int expected_m, void *stream);
+
+/*
+ * Packs power-of-two fp32 scales into the words above (the pages' library
+ * offers a scale layout transform, transform_sf_into_required_layout, among
+ * its utilities: "Utilities and environment variables").  sf is viewed as
+ * fp32 [outer][kblocks][inner], out as uint32 [outer][ceil(kblocks/4)][inner];
+ * byte j of out[o][q][i] = bits 23..30 of sf[o][4q+j][i], 0 where 4q+j >=
+ * kblocks.  For sfa: outer = groups (1 when dense), kblocks = K/128, inner =
+ * the scale leading dimension; for sfb: outer = G * ceil(N/128), kblocks =
+ * K/128, inner = 1.  sf and out device memory, 4-byte aligned, not
+ * overlapping; enqueued on `stream`.
+ * Errors: DG_ERR_NULL (sf, out), DG_ERR_SHAPE (outer, kblocks, inner < 1;
+ * more than 2^31 workgroups), DG_ERR_ALIGN, DG_ERR_HIP.
+ */
+int dg_pack_sf_ue8m0(const float *sf, int outer, int kblocks, int inner,
+                     uint32_t *out, void *stream);
+
+/*
  * FP8 MQA logits, non-paged (the DeepSeek v3.2 indexer's scoring kernel;
  * GeekNews summary of the DeepGEMM README, section on the MQA kernels for the
  * v3.2 Indexer).  For every query token i and key token j in

@@ -77,6 +77,18 @@ EXPORTS = {
     "dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                                              ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_int,
                                                              ct.c_int, ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_fp8_gemm_nt_ue8m0_packed": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_void_p,
+                                               ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int,
+                                               ct.c_void_p, ct.c_size_t, ct.c_void_p]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                                    ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                                    ct.c_void_p, ct.c_int, ct.c_int, ct.c_int,
+                                                                    ct.c_int, ct.c_void_p]),
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                                ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                                ct.c_void_p, ct.c_int, ct.c_int, ct.c_int,
+                                                                ct.c_int, ct.c_int, ct.c_void_p]),
+    "dg_pack_sf_ue8m0": (ct.c_int, [ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_void_p, ct.c_void_p]),
     "dg_fp8_mqa_logits": (ct.c_int, [ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                      ct.c_void_p, ct.c_int, ct.c_void_p, ct.c_int, ct.c_int, ct.c_int, ct.c_int,
                                      ct.c_void_p]),
@@ -310,6 +322,80 @@ def quantize_e4m3_128x128(x, q=None, sf=None, ue8m0=False):
     name = _name("dg_quantize_e4m3_128x128", ue8m0)
     _check(getattr(lib(), name)(*args), name)
     return q, sf
+
+
+def pack_sf_ue8m0(sf, k_axis, out=None):
+    """Packs power-of-two fp32 scales four per 32-bit word along the K-block axis `k_axis`
+    (dg_pack_sf_ue8m0): byte j of word q holds the exponent field of K block 4q + j.  sfa [.., K/128, ld]
+    takes k_axis=-2, sfb [.., ceil(N/128), K/128] k_axis=-1.  Returns int32 words of sf's shape with
+    ceil(K/512) along k_axis."""
+    shape = tuple(sf.shape)
+    ax = k_axis % len(shape)
+    outer = 1
+    for v in shape[:ax]:
+        outer *= v
+    inner = 1
+    for v in shape[ax + 1:]:
+        inner *= v
+    kblocks = shape[ax]
+    out_shape = shape[:ax] + (ceil_div(kblocks, 4),) + shape[ax + 1:]
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.int32, device=sf.device)
+    _check(lib().dg_pack_sf_ue8m0(_ptr(sf, torch.float32, "sf"), outer, kblocks, inner,
+                                  _ptr(out, torch.int32, "out", out_shape), _stream(sf)), "dg_pack_sf_ue8m0")
+    return out
+
+
+def fp8_gemm_nt_ue8m0_packed(a, sfa, b, sfb, d, c=None, workspace="auto"):
+    """D = C + A . B^T on packed power-of-two scales (dg_fp8_gemm_nt_ue8m0_packed): sfa int32
+    [ceil(K/512), ld_sfa], sfb int32 [ceil(N/128), ceil(K/512)] as pack_sf_ue8m0 writes them; the other
+    arguments as for fp8_gemm_nt (workspace None: no split-K)."""
+    M, K = a.shape
+    N = b.shape[0]
+    nkw = ceil_div(K // 128, 4)
+    if sfa.dim() != 2 or sfa.shape[0] != nkw:
+        raise ValueError(f"sfa: shape {tuple(sfa.shape)}, expected [ceil(K/512)={nkw}, ld_sfa]")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace {workspace!r}")
+        workspace = get_workspace(M, N, K, d.device)
+    ws = _ptr(workspace, torch.uint8, "workspace")
+    args = (_ptr(a, _FP8, "a", (M, K)), _ptr(sfa, torch.int32, "sfa"), int(sfa.shape[1]),
+            _ptr(b, _FP8, "b", (N, K)), _ptr(sfb, torch.int32, "sfb", (ceil_div(N, 128), nkw)),
+            _ptr(c, torch.bfloat16, "c", (M, N)), _ptr(d, torch.bfloat16, "d", (M, N)), M, N, K,
+            ws, int(workspace.numel()) if workspace is not None else 0, _stream(d))
+    _check(lib().dg_fp8_gemm_nt_ue8m0_packed(*args), "dg_fp8_gemm_nt_ue8m0_packed")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed(a, sfa, b, sfb, d, m_indices, c=None):
+    """Contiguous grouped GEMM on packed power-of-two scales: sfa int32 [ceil(K/512), M_total], sfb int32
+    [G, ceil(N/128), ceil(K/512)]; the rest as m_grouped_fp8_gemm_nt_contiguous."""
+    M_total, K = a.shape
+    G, N, _ = b.shape
+    nkw = ceil_div(K // 128, 4)
+    args = (_ptr(a, _FP8, "a", (M_total, K)), _ptr(sfa, torch.int32, "sfa", (nkw, M_total)),
+            _ptr(b, _FP8, "b", (G, N, K)), _ptr(sfb, torch.int32, "sfb", (G, ceil_div(N, 128), nkw)),
+            _ptr(c, torch.bfloat16, "c", (M_total, N)), _ptr(d, torch.bfloat16, "d", (M_total, N)),
+            _ptr(m_indices, torch.int32, "m_indices", (M_total,)), M_total, N, K, G, _stream(d))
+    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed(*args),
+           "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked_ue8m0_packed(a, sfa, b, sfb, d, masked_m, expected_m=0, c=None):
+    """Masked grouped GEMM on packed power-of-two scales: sfa int32 [G, ceil(K/512), round_up(M_cap,4)],
+    sfb int32 [G, ceil(N/128), ceil(K/512)]; the rest as m_grouped_fp8_gemm_nt_masked."""
+    G, M_cap, K = a.shape
+    N = b.shape[1]
+    ld = (M_cap + 3) // 4 * 4
+    nkw = ceil_div(K // 128, 4)
+    args = (_ptr(a, _FP8, "a", (G, M_cap, K)), _ptr(sfa, torch.int32, "sfa", (G, nkw, ld)),
+            _ptr(b, _FP8, "b", (G, N, K)), _ptr(sfb, torch.int32, "sfb", (G, ceil_div(N, 128), nkw)),
+            _ptr(c, torch.bfloat16, "c", (G, M_cap, N)), _ptr(d, torch.bfloat16, "d", (G, M_cap, N)),
+            _ptr(masked_m, torch.int32, "masked_m", (G,)), G, M_cap, N, K, int(expected_m), _stream(d))
+    _check(lib().dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed(*args), "dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed")
+    return d
 
 
 def fp8_mqa_logits(q, kv, kv_scale, weights, k_start, k_end, clean_logits=True, logits=None):

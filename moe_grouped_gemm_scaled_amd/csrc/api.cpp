@@ -120,7 +120,7 @@ extern "C" {
 
 static int gemm_nt_impl(const uint8_t *a, const float *sfa, int ld_sfa, const uint8_t *b, const float *sfb,
                         const uint16_t *c, uint16_t *d, int M, int N, int K, void *workspace,
-                        size_t workspace_bytes, void *stream, bool ue8m0) {
+                        size_t workspace_bytes, void *stream, bool ue8m0, bool packed = false) {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_NULL;
     if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (ld_sfa < M || ld_sfa % 4 != 0) return DG_ERR_ALIGN;
@@ -128,6 +128,7 @@ static int gemm_nt_impl(const uint8_t *a, const float *sfa, int ld_sfa, const ui
         (c && !aligned16(c)) || (workspace && !aligned16(workspace)))
         return DG_ERR_ALIGN;
     dg::GemmProblem p{a, sfa, b, sfb, c, d, nullptr, M, N, K, ld_sfa, 1, dg::Mode::Dense, 0, ue8m0};
+    p.packed = packed;
     p.ws = workspace;
     p.ws_bytes = workspace ? workspace_bytes : 0;
     return run_gemm(p, stream);
@@ -135,19 +136,20 @@ static int gemm_nt_impl(const uint8_t *a, const float *sfa, int ld_sfa, const ui
 
 static int contiguous_impl(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb,
                            const uint16_t *c, uint16_t *d, const int32_t *m_indices, int M_total, int N, int K,
-                           int G, void *stream, bool ue8m0) {
+                           int G, void *stream, bool ue8m0, bool packed = false) {
     if (!a || !sfa || !b || !sfb || !d || !m_indices) return DG_ERR_NULL;
     if (M_total < 1 || M_total % 128 != 0 || N < 1 || G < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
         !aligned16(m_indices) || (c && !aligned16(c)))
         return DG_ERR_ALIGN;
     dg::GemmProblem p{a, sfa, b, sfb, c, d, m_indices, M_total, N, K, M_total, G, dg::Mode::Contig, 0, ue8m0};
+    p.packed = packed;
     return run_gemm(p, stream);
 }
 
 static int masked_impl(const uint8_t *a, const float *sfa, const uint8_t *b, const float *sfb, const uint16_t *c,
                        uint16_t *d, const int32_t *masked_m, int G, int M_cap, int N, int K, int expected_m,
-                       void *stream, bool ue8m0) {
+                       void *stream, bool ue8m0, bool packed = false) {
     if (!a || !sfa || !b || !sfb || !d || !masked_m) return DG_ERR_NULL;
     if (G < 1 || M_cap < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
@@ -155,6 +157,7 @@ static int masked_impl(const uint8_t *a, const float *sfa, const uint8_t *b, con
         return DG_ERR_ALIGN;
     const int ld = (M_cap + 3) / 4 * 4;
     dg::GemmProblem p{a, sfa, b, sfb, c, d, masked_m, M_cap, N, K, ld, G, dg::Mode::Masked, expected_m, ue8m0};
+    p.packed = packed;
     return run_gemm(p, stream);
 }
 
@@ -293,16 +296,65 @@ int dg_fp8_gemm_nt_noalloc(const uint8_t *a, const float *sfa, int ld_sfa, const
     return gemm_nt_noalloc_impl(a, sfa, ld_sfa, b, sfb, c, d, M, N, K, stream, false);
 }
 
+// Packed power-of-two scales (four UE8M0 exponents per 32-bit word along the
+// K blocks): the NT GEMM and its grouped forms on the pipelined family.  The
+// words are carried in the fp32 scale pointers of the problem.
+// The pipelined kernels address an operand with 32-bit buffer offsets.
+static const float *words(const uint32_t *w) { return reinterpret_cast<const float *>(w); }
+static bool offsets_fit(int rows, int N, int K) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (int64_t)rows * K < lim && (int64_t)N * K < lim;
+}
+
+int dg_fp8_gemm_nt_ue8m0_packed(const uint8_t *a, const uint32_t *sfa, int ld_sfa, const uint8_t *b,
+                                const uint32_t *sfb, const uint16_t *c, uint16_t *d, int M, int N, int K,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    if (!offsets_fit(M, N, K)) return DG_ERR_SHAPE;
+    return gemm_nt_impl(a, words(sfa), ld_sfa, b, words(sfb), c, d, M, N, K, workspace, workspace_bytes, stream,
+                        true, true);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed(const uint8_t *a, const uint32_t *sfa, const uint8_t *b,
+                                                     const uint32_t *sfb, const uint16_t *c, uint16_t *d,
+                                                     const int32_t *m_indices, int M_total, int N, int K, int G,
+                                                     void *stream) {
+    if (!offsets_fit(M_total, N, K)) return DG_ERR_SHAPE;
+    return contiguous_impl(a, words(sfa), b, words(sfb), c, d, m_indices, M_total, N, K, G, stream, true, true);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed(const uint8_t *a, const uint32_t *sfa, const uint8_t *b,
+                                                 const uint32_t *sfb, const uint16_t *c, uint16_t *d,
+                                                 const int32_t *masked_m, int G, int M_cap, int N, int K,
+                                                 int expected_m, void *stream) {
+    if (!offsets_fit(M_cap, N, K)) return DG_ERR_SHAPE;
+    return masked_impl(a, words(sfa), b, words(sfb), c, d, masked_m, G, M_cap, N, K, expected_m, stream, true,
+                       true);
+}
+
+int dg_pack_sf_ue8m0(const float *sf, int outer, int kblocks, int inner, uint32_t *out, void *stream) {
+    if (!sf || !out) return DG_ERR_NULL;
+    if (outer < 1 || kblocks < 1 || inner < 1) return DG_ERR_SHAPE;
+    if ((int64_t)outer * ((kblocks + 3) / 4) * inner > (int64_t)0x7fffffff * 256) return DG_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(sf) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u)) return DG_ERR_ALIGN;
+    int dev = 0, cus = 0;
+    const int st = current_device(dev, cus);
+    if (st != DG_OK) return st;
+    return dg::launch_pack_ue8m0(sf, outer, kblocks, inner, out, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? DG_OK
+               : DG_ERR_HIP;
+}
+
 int64_t dg_get_workspace_size(int M, int N, int K) {
     if (M < 1 || N < 1 || check_k(K) != DG_OK) return DG_ERR_SHAPE;
     int dev = 0, cus = 0;
     const int st = current_device(dev, cus);
     if (st != DG_OK) return st;
-    // the largest need over both scale forms (the same tiles and splits today)
+    // the largest need over the scale forms (fp32, power-of-two, packed)
     size_t need = 0;
-    for (int ue = 0; ue < 2; ++ue) {
+    for (int form = 0; form < 3; ++form) {
         dg::GemmProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K,
-                          (M + 3) / 4 * 4, 1, dg::Mode::Dense, 0, ue != 0};
+                          (M + 3) / 4 * 4, 1, dg::Mode::Dense, 0, form != 0};
+        p.packed = form == 2;
         size_t n = 0;
         const int ps = plan_scratch(p, cus, n);
         if (ps != DG_OK) return ps;

@@ -10,6 +10,12 @@
 
 namespace dg {
 
+// Packs the exponent fields of power-of-two fp32 scales, viewed as
+// sf[outer][kblocks][inner], four K blocks per 32-bit word:
+// out[outer][ceil(kblocks/4)][inner], byte j of word q = exponent of K block
+// 4q + j (0 past the last K block).
+hipError_t launch_pack_ue8m0(const float *sf, int outer, int kblocks, int inner, uint32_t *out, hipStream_t stream);
+
 // ue8m0: the block scale rounded up to a power of two
 hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
                               int ld_sf, hipStream_t stream, bool ue8m0);
@@ -49,6 +55,10 @@ struct GemmProblem {
     // dense only: A stored MN-major as [K][M] (TN, TT layouts), B as [K][N]
     // (NN, TN); only the pipelined family takes these
     bool a_mn = false, b_mn = false;
+    // power-of-two scales packed four UE8M0 exponents per 32-bit word along
+    // the K blocks (sfa, sfb then point at uint32 words); the pipelined family
+    // only
+    bool packed = false;
     // K-grouped only: fp32 C (or NULL) and D
     const float *c32 = nullptr;
     float *d32 = nullptr;

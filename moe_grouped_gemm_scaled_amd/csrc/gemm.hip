@@ -274,9 +274,9 @@ static hipError_t launch_tiled(const GemmProblem &p, hipStream_t stream, std::st
 }
 
 hipError_t launch_gemm(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
-    // MN-major operands (NN, TN, TT layouts): the pipelined family only,
-    // whatever the family setting
-    if (p.a_mn || p.b_mn) return launch_pipe(p, num_cus, stream, config);
+    // MN-major operands (NN, TN, TT layouts) and packed power-of-two scales:
+    // the pipelined family only, whatever the family setting
+    if (p.a_mn || p.b_mn || p.packed) return pipe_eligible(p) ? launch_pipe(p, num_cus, stream, config) : hipErrorInvalidValue;
     const int f = kernel_family_setting();
     if (f == 1 && skinny_eligible(p)) return launch_skinny(p, num_cus, stream, config);
     if (f == 5 && stream_eligible(p)) return launch_stream(p, num_cus, stream, config);

@@ -136,8 +136,11 @@ __device__ __forceinline__ int mn_swizzle(int r) {
 // AMN / BMN: A (B) is stored MN-major, as [K][M] ([K][N]); its LDS tiles
 // then hold K rows of BM (BN) bytes and fragments are read with transposing
 // LDS loads (read_frag_tr).
+// PK: power-of-two scales packed four UE8M0 exponents per 32-bit word along
+// the K blocks (byte j of word q holds the exponent of K block 4q + j):
+// sfa [K/512 rounded up][ld_sfa], sfb [ceil(N/128)][K/512 rounded up].
 template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false,
-          bool AMN = false, bool BMN = false>
+          bool AMN = false, bool BMN = false, bool PK = false>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 pipe_kernel(PipeParams p) {
     constexpr int NW = WGM * WGN;
@@ -171,6 +174,7 @@ pipe_kernel(PipeParams p) {
     static_assert(MODE != Mode::KGrouped || (AMN && BMN && KS == 1 && !SPLIT),
                   "K-grouped: both operands MN-major, one K block per stage, no split-K");
     constexpr bool KG = MODE == Mode::KGrouped;
+    static_assert(!PK || (UE && !KG && !AMN && !BMN), "packed scales: power-of-two scales, NT operand layouts");
     static_assert(NW % 2 == 0 && (NW / 2) * EPI_ROWS * EPI_PITCH * 4 <= STAGE,
                   "epilogue staging: half the waves per stage");
 
@@ -258,6 +262,7 @@ pipe_kernel(PipeParams p) {
     }
     const int nblk = st1 - st0;                    // steps (K-grouped: may be 0)
 
+    const int nkw = PK ? (nkb + 3) / 4 : nkb;      // scale rows of sfa, scale entries per sfb row
     const uint8_t *A = p.a;
     const float *SFA = p.sfa;
     const uint8_t *B = p.b;
@@ -273,9 +278,9 @@ pipe_kernel(PipeParams p) {
         if (m0 >= mm) return;                      // uniform exit, before any barrier
         valid_m = mm;
         A += (int64_t)grp * rows_a * K;
-        SFA += (int64_t)grp * nkb * ld;
+        SFA += (int64_t)grp * nkw * ld;
         B += (int64_t)grp * N * K;
-        SFB += (int64_t)grp * nnb * nkb;
+        SFB += (int64_t)grp * nnb * nkw;
         if (C) C += (int64_t)grp * rows_a * N;
         D += (int64_t)grp * rows_a * N;
     }
@@ -284,7 +289,7 @@ pipe_kernel(PipeParams p) {
         expert = p.idx[m0];
         if (expert < 0 || expert >= p.G) return;   // padding (or an invalid id): uniform exit
         B += (int64_t)expert * N * K;
-        SFB += (int64_t)expert * nnb * nkb;
+        SFB += (int64_t)expert * nnb * nkw;
     }
 
     const int tid = threadIdx.x;
@@ -351,22 +356,27 @@ pipe_kernel(PipeParams p) {
     // into unused slots.
     // K-grouped: B scales are per column (sfb[kb][n]); lane l of a B-scale
     // wave fetches sfb[kb][n0 + 4l .. +3] (clamped to the last 4 columns).
+    // Packed scales (PK): wave w < KS fetches the words of K block kb + w
+    // (row (kb + w)/4 of the packed sfa), B-scale waves the 4 words from
+    // (kb/4) of their scale row: K blocks 4(kb/4) .. +15, which hold every K
+    // block of the step.
     const bool wsa = wave < KS;
     const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
-        wsa ? (void *)SFA : (void *)SFB, (short)0, wsa ? nkb * ld * 4 : (KG ? nkb * N * 4 : nnb * nkb * 4),
+        wsa ? (void *)SFA : (void *)SFB, (short)0, wsa ? nkw * ld * 4 : (KG ? nkb * N * 4 : nnb * nkw * 4),
         0x00020000);
     const int sa_row = m0 + 4 * lane;
-    const int v_s = wsa ? ((sa_row < ld ? sa_row : 0) + wave * ld) * 4
-                        : (KG ? min(n0 + 4 * lane, N - 4) * 4 : min(n0 / 128 + lane, nnb - 1) * nkb * 4);
+    const int v_s = wsa ? ((sa_row < ld ? sa_row : 0) + (PK ? 0 : wave * ld)) * 4
+                        : (KG ? min(n0 + 4 * lane, N - 4) * 4 : min(n0 / 128 + lane, nnb - 1) * nkw * 4);
     const int lds_s = wsa ? OFF_SA + wave * 1024 : OFF_SB;
     const int s_stride = wsa ? ld * 4 : (KG ? N * 4 : 4);
 
     // DMA of step st (K blocks KS*st .. +KS-1) into stage stg
     auto dma = [&](uint8_t *stg, int st) __attribute__((always_inline)) {
         const int kb = st * KS;
+        const int s_off = PK ? (wsa ? ((kb + wave) >> 2) * ld * 4 : (kb >> 2) * 4) : kb * s_stride;
         dma_step<DA, DB, RG_STEP * 1024, RG_STEP * 1024>(stg, rA, rB, rS, va, vb, v_s, lds_a, lds_b, lds_s,
                                                          AMN ? kb * kKBlock * p.lda : kb * kKBlock,
-                                                         BMN ? kb * kKBlock * p.ldb : kb * kKBlock, kb * s_stride);
+                                                         BMN ? kb * kKBlock * p.ldb : kb * kKBlock, s_off);
     };
 
     v4f acc[SM][SN];
@@ -528,10 +538,18 @@ pipe_kernel(PipeParams p) {
     // fresh partial per K block and no promotion on the VALU.
     // K-grouped: the first operand's exponent is per lane too, from the
     // scale of the B column (row of the B fragment) the lane holds.
-    auto compute_block_ue = [&](const uint8_t *stg_step, auto kkc) __attribute__((always_inline)) {
+    // Packed scales: the exponent of K block kb + kk is byte (kb + kk) & 3 of
+    // its word.
+    auto compute_block_ue = [&](const uint8_t *stg_step, auto kkc, int kb) __attribute__((always_inline)) {
         constexpr int kk = decltype(kkc)::value;
-        const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
-        const int eb = (int)(__float_as_uint(sb) >> 23);
+        int eb;
+        if constexpr (PK) {
+            const uint32_t wb = reinterpret_cast<const uint32_t *>(stg_step + off_sb)[((kb & 3) + kk) >> 2];
+            eb = (int)((wb >> (8 * ((kb + kk) & 3))) & 0xffu);
+        } else {
+            const float sb = *reinterpret_cast<const float *>(stg_step + off_sb + 4 * kk);
+            eb = (int)(__float_as_uint(sb) >> 23);
+        }
         int ebj[KG ? SN : 1];
         if constexpr (KG) {
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
@@ -564,8 +582,14 @@ pipe_kernel(PipeParams p) {
                 const v4i hi = *reinterpret_cast<const v4i *>(stg + off_a0[1] + i * 16 * kKBlock);
                 af = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             }
-            const float sa = *reinterpret_cast<const float *>(stg_s + off_sa0 + i * 64);
-            const int ea = (int)(__float_as_uint(sa) >> 23);
+            int ea;
+            if constexpr (PK) {
+                const uint32_t wa = *reinterpret_cast<const uint32_t *>(stg_s + off_sa0 + i * 64);
+                ea = (int)((wa >> (8 * ((kb + kk) & 3))) & 0xffu);
+            } else {
+                const float sa = *reinterpret_cast<const float *>(stg_s + off_sa0 + i * 64);
+                ea = (int)(__float_as_uint(sa) >> 23);
+            }
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
                 acc[i][j] = mfma_16x16x128_e4m3_scaled(bf[j], af, acc[i][j], KG ? ebj[KG ? j : 0] : eb, ea);
@@ -573,9 +597,10 @@ pipe_kernel(PipeParams p) {
         });
     };
 
-    auto compute = [&](const uint8_t *stg) __attribute__((always_inline)) {
+    // multiply step st (its first K block is st * KS)
+    auto compute = [&](const uint8_t *stg, int st) __attribute__((always_inline)) {
         static_for<KS>([&](auto kkc) __attribute__((always_inline)) {
-            if constexpr (UE) compute_block_ue(stg, kkc);
+            if constexpr (UE) compute_block_ue(stg, kkc, st * KS);
             else compute_block(stg, kkc);
         });
     };
@@ -598,7 +623,7 @@ pipe_kernel(PipeParams p) {
                 __builtin_amdgcn_s_waitcnt(kWaitPipe);
                 lds_barrier();
                 dma(stage_of(sc), st0 + min(j + NST - 1, nblk - 1));
-                if (j >= 0 && wave_live) compute(stage_of(std::integral_constant<int, (u + 1) % NST>{}));
+                if (j >= 0 && wave_live) compute(stage_of(std::integral_constant<int, (u + 1) % NST>{}), st0 + j);
             });
         }
     }
@@ -755,7 +780,7 @@ bool pipe_eligible(const GemmProblem &p) {
 // so that exactly `units` workgroups run), each split keeping at least one
 // step; otherwise, or when no workspace is available, there is no split.
 template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool DEEP, Mode MODE, bool SPLIT, bool UE = false,
-          bool AMN = false, bool BMN = false>
+          bool AMN = false, bool BMN = false, bool PK = false>
 hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, std::string &config) {
     PipeParams k;
     k.a = p.a; k.sfa = p.sfa; k.b = p.b; k.sfb = p.sfb; k.c = p.c; k.d = p.d; k.idx = p.idx;
@@ -808,23 +833,23 @@ hipError_t launch_pipe_t(const GemmProblem &p, int units, hipStream_t stream, st
              "family=pipe mode=%d tile=%dx%dx128 waves=%dx%d stages=%d kblocks_per_stage=%d deep=%d splits=%d%s "
              "grid=%lld%s%s",
              (int)MODE, BM, BN, WGM, WGN, NST, KS, (int)DEEP, split ? k.splits_lo : 1,
-             split && k.split_hi > 0 ? "+" : "", (long long)grid, UE ? " scales=ue8m0" : "",
+             split && k.split_hi > 0 ? "+" : "", (long long)grid, UE ? (PK ? " scales=ue8m0_packed" : " scales=ue8m0") : "",
              AMN ? (BMN ? " layout=tn" : " layout=tt") : (BMN ? " layout=nn" : ""));
     config = buf;
     if (p.plan) return hipSuccess;
     if constexpr (SPLIT) {
         if (split) {
-            hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true, UE, AMN, BMN>),
+            hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, true, UE, AMN, BMN, PK>),
                                dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, stream, k);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, false, UE, AMN, BMN>),
+    hipLaunchKernelGGL((pipe_kernel<BM, BN, WGM, WGN, NST, KS, DEEP, MODE, false, UE, AMN, BMN, PK>),
                        dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, stream, k);
     return hipGetLastError();
 }
 
-template <bool UE>
+template <bool UE, bool PK = false>
 static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     const int cus = num_cus > 0 ? num_cus : 256;
     const int nkb = p.K / kKBlock;
@@ -835,17 +860,17 @@ static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t 
         // (N, K) in {(2112, 7168), (7168, 16384)})
         if (p.rows_a <= 64) {
             if (nkb % 2 == 0) {
-                if (p.N < 4096) return launch_pipe_t<64, 64, 2, 4, 2, 2, false, Mode::Dense, true, UE>(p, cus, stream, config);
-                return launch_pipe_t<64, 128, 2, 4, 3, 2, false, Mode::Dense, true, UE>(p, cus, stream, config);
+                if (p.N < 4096) return launch_pipe_t<64, 64, 2, 4, 2, 2, false, Mode::Dense, true, UE, false, false, PK>(p, cus, stream, config);
+                return launch_pipe_t<64, 128, 2, 4, 3, 2, false, Mode::Dense, true, UE, false, false, PK>(p, cus, stream, config);
             }
-            return launch_pipe_t<64, 128, 2, 4, 4, 1, false, Mode::Dense, true, UE>(p, cus, stream, config);
+            return launch_pipe_t<64, 128, 2, 4, 4, 1, false, Mode::Dense, true, UE, false, false, PK>(p, cus, stream, config);
         }
         if (p.rows_a <= 128) {
             if (nkb % 2 == 0) {
-                if (p.N < 4096) return launch_pipe_t<128, 64, 4, 2, 3, 2, true, Mode::Dense, true, UE>(p, cus, stream, config);
-                return launch_pipe_t<128, 128, 2, 4, 2, 2, true, Mode::Dense, true, UE>(p, cus, stream, config);
+                if (p.N < 4096) return launch_pipe_t<128, 64, 4, 2, 3, 2, true, Mode::Dense, true, UE, false, false, PK>(p, cus, stream, config);
+                return launch_pipe_t<128, 128, 2, 4, 2, 2, true, Mode::Dense, true, UE, false, false, PK>(p, cus, stream, config);
             }
-            return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true, UE>(p, cus, stream, config);
+            return launch_pipe_t<128, 128, 2, 4, 4, 1, true, Mode::Dense, true, UE, false, false, PK>(p, cus, stream, config);
         }
         // prefill shapes: 256x256 tiles (8 waves of 128x64, two stages) read
         // the fewest bytes from LDS and from L2 per MFMA.  With streaming D
@@ -853,18 +878,18 @@ static hipError_t launch_pipe_ue(const GemmProblem &p, int num_cus, hipStream_t 
         // measured shape (MI355X, M = 4096, (N, K) in {(4096, 7168): 107 us,
         // (7168, 2048): 77 against 92 us for 128x128, (24576, 1536): 208 us}).
         if (p.rows_a >= 256)
-            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, UE>(p, 0, stream, config);
-        return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, UE>(p, 0, stream, config);
+            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Dense, false, UE, false, false, PK>(p, 0, stream, config);
+        return launch_pipe_t<128, 128, 2, 4, 2, 1, true, Mode::Dense, false, UE, false, false, PK>(p, 0, stream, config);
     }
     case Mode::Contig:
         // 256-row units that never mix experts (the segments are 128-row
         // aligned); measured on MI355X for 8 experts, N = 4096, K = 7168:
         // 540 us against 575 us with 128x256 tiles
         if (p.rows_a >= 256)
-            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Contig, false, UE>(p, 0, stream, config);
-        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false, UE>(p, 0, stream, config);
+            return launch_pipe_t<256, 256, 2, 4, 2, 1, true, Mode::Contig, false, UE, false, false, PK>(p, 0, stream, config);
+        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Contig, false, UE, false, false, PK>(p, 0, stream, config);
     case Mode::Masked:
-        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false, UE>(p, 0, stream, config);
+        return launch_pipe_t<128, 256, 2, 4, 3, 1, true, Mode::Masked, false, UE, false, false, PK>(p, 0, stream, config);
     case Mode::KGrouped: break;                    // launched by launch_pipe
     }
     return hipErrorInvalidValue;
@@ -907,6 +932,7 @@ hipError_t launch_pipe(const GemmProblem &p, int num_cus, hipStream_t stream, st
         if (p.a_mn) return launch_pipe_layout<true, false, false>(p, num_cus, stream, config);
         return launch_pipe_layout<false, true, false>(p, num_cus, stream, config);
     }
+    if (p.packed) return p.ue8m0 ? launch_pipe_ue<true, true>(p, num_cus, stream, config) : hipErrorInvalidValue;
     return p.ue8m0 ? launch_pipe_ue<true>(p, num_cus, stream, config) : launch_pipe_ue<false>(p, num_cus, stream, config);
 }
 

@@ -139,6 +139,34 @@ quant_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float
     if (t == 0) sf[(g * nrb + rb) * (int64_t)nkb + kb] = s;
 }
 
+// Packing of power-of-two scales into UE8M0 words: thread per output word.
+__global__ void __launch_bounds__(256)
+pack_ue8m0_kernel(const float *__restrict__ sf, int kblocks, int inner, int words, uint32_t *__restrict__ out,
+                  int64_t total) {
+    const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (w >= total) return;
+    const int i = (int)(w % inner);
+    const int64_t r = w / inner;
+    const int q = (int)(r % words);
+    const int64_t o = r / words;
+    const float *src = sf + (o * kblocks + 4 * q) * (int64_t)inner + i;
+    uint32_t v = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (4 * q + j < kblocks) v |= ((__float_as_uint(src[(int64_t)j * inner]) >> 23) & 0xffu) << (8 * j);
+    out[w] = v;
+}
+
+hipError_t launch_pack_ue8m0(const float *sf, int outer, int kblocks, int inner, uint32_t *out, hipStream_t stream) {
+    const int words = (kblocks + 3) / 4;
+    const int64_t total = (int64_t)outer * words * inner;
+    const int64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_ue8m0_kernel, dim3((unsigned)grid), dim3(256), 0, stream, sf, kblocks, inner, words, out,
+                       total);
+    return hipGetLastError();
+}
+
 template <int U>
 static hipError_t launch_quant_1x128_u(const float *x, int groups, int rows, int nkb, uint8_t *q, float *sf,
                                        int ld_sf, hipStream_t stream, bool ue8m0) {

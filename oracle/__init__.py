@@ -53,6 +53,10 @@ def _load():
         "orc_k_grouped_tn_at": (None, [P, P, P, P, P, P, I, I, I, P, P, P, L, P]),
         "orc_mqa_logits": (None, [P, P, P, P, P, P, I, I, I, I, I, P]),
         "orc_mqa_logits_rows": (None, [P, P, P, P, P, P, I, I, I, I, P, I, P]),
+        "orc_ue8m0_encode": (_ct.c_uint8, [_ct.c_float]),
+        "orc_ue8m0_decode": (D, [_ct.c_uint8]),
+        "orc_pack_ue8m0": (None, [P, I, I, I, P]),
+        "orc_unpack_ue8m0": (None, [P, I, I, I, P]),
         "orc_num_threads": (I, []),
         "orc_set_num_threads": (None, [I]),
     }
@@ -322,6 +326,40 @@ def mqa_logits_rows(q, kv, kv_scale, weights, k_start, k_end, clean_logits, rows
     _load().orc_mqa_logits_rows(q.ctypes.data, kv.ctypes.data, kv_scale.ctypes.data, weights.ctypes.data,
                                 k_start.ctypes.data, k_end.ctypes.data, int(bool(clean_logits)), H, D, Skv,
                                 rows.ctypes.data, rows.size, out.ctypes.data)
+    return out
+
+
+def ue8m0_encode(s):
+    return int(_load().orc_ue8m0_encode(float(s)))
+
+
+def ue8m0_decode(e):
+    return float(_load().orc_ue8m0_decode(int(e)))
+
+
+def _axis_split(shape, k_axis):
+    ax = k_axis % len(shape)
+    outer = int(_np.prod(shape[:ax], dtype=_np.int64))
+    inner = int(_np.prod(shape[ax + 1:], dtype=_np.int64))
+    return ax, outer, shape[ax], inner
+
+
+def pack_ue8m0(sf, k_axis):
+    """Power-of-two fp32 scales -> uint32 words, four K blocks per word along `k_axis`
+    (-2 for sfa [.., K/128, ld], -1 for sfb [.., ceil(N/128), K/128])."""
+    sf = _np.ascontiguousarray(sf, dtype=_np.float32)
+    ax, outer, kb, inner = _axis_split(sf.shape, k_axis)
+    out = _np.empty(sf.shape[:ax] + ((kb + 3) // 4,) + sf.shape[ax + 1:], dtype=_np.uint32)
+    _load().orc_pack_ue8m0(_p(sf, _np.float32), outer, kb, inner, _p(out, _np.uint32))
+    return out
+
+
+def unpack_ue8m0(w, kblocks, k_axis):
+    """uint32 words -> the fp32 scales they encode ([.., kblocks, ..] along `k_axis`)."""
+    w = _np.ascontiguousarray(w, dtype=_np.uint32)
+    ax, outer, _, inner = _axis_split(w.shape, k_axis)
+    out = _np.empty(w.shape[:ax] + (kblocks,) + w.shape[ax + 1:], dtype=_np.float32)
+    _load().orc_unpack_ue8m0(_p(w, _np.uint32), outer, kblocks, inner, _p(out, _np.float32))
     return out
 
 

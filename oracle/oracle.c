@@ -126,6 +126,50 @@ float orc_block_scale_ue8m0(float amax)
     return m == 0.5f ? s : ldexpf(1.0f, e);
 }
 
+/* UE8M0 code of a power of two: frexp writes s = 0.5 * 2^e, so log2 s =
+ * e - 1 and the biased code is e - 1 + 127. */
+uint8_t orc_ue8m0_encode(float s)
+{
+    int e;
+    frexp((double)s, &e);
+    return (uint8_t)(e - 1 + 127);
+}
+
+double orc_ue8m0_decode(uint8_t e)
+{
+    return ldexp(1.0, (int)e - 127);
+}
+
+void orc_pack_ue8m0(const float *sf, int outer, int kblocks, int inner, uint32_t *w)
+{
+    const int words = (kblocks + 3) / 4;
+    for (int o = 0; o < outer; ++o)
+        for (int q = 0; q < words; ++q)
+            for (int i = 0; i < inner; ++i) {
+                uint32_t v = 0;
+                for (int j = 0; j < 4; ++j) {
+                    const int kb = 4 * q + j;
+                    if (kb < kblocks) {
+                        const float s = sf[((size_t)o * kblocks + kb) * inner + i];
+                        v += (uint32_t)orc_ue8m0_encode(s) * (1u << (8 * j));
+                    }
+                }
+                w[((size_t)o * words + q) * inner + i] = v;
+            }
+}
+
+void orc_unpack_ue8m0(const uint32_t *w, int outer, int kblocks, int inner, float *sf)
+{
+    const int words = (kblocks + 3) / 4;
+    for (int o = 0; o < outer; ++o)
+        for (int kb = 0; kb < kblocks; ++kb)
+            for (int i = 0; i < inner; ++i) {
+                const uint32_t v = w[((size_t)o * words + kb / 4) * inner + i];
+                const uint8_t e = (uint8_t)((v / (1u << (8 * (kb % 4)))) % 256u);
+                sf[((size_t)o * kblocks + kb) * inner + i] = (float)orc_ue8m0_decode(e);
+            }
+}
+
 static float block_scale_mode(float amax, int ue8m0)
 {
     return ue8m0 ? orc_block_scale_ue8m0(amax) : orc_block_scale(amax);

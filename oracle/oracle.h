@@ -167,6 +167,22 @@ void orc_mqa_logits_rows(const uint8_t *q, const uint8_t *kv, const float *kv_sc
                          const int32_t *k_start, const int32_t *k_end, int clean_logits,
                          int H, int D, int Skv, const int32_t *rows, int nrows, double *out);
 
+/* Packed UE8M0 scales (GeekNews summary of the DeepGEMM README, section
+ * "GEMM interface and layout constraints": the SM100 kernels take four UE8M0
+ * scaling factors packed into one 32-bit integer).  A UE8M0 byte e is the
+ * unsigned power-of-two exponent: it stands for 2^(e - 127).  The pages do
+ * not fix which four scales share a word; the reading here: four consecutive
+ * K blocks of one row (A) or 128-column block (B), K block 4q + j in bits
+ * 8j .. 8j+7 of word q, unused high bytes 0.
+ *   sf [outer][kblocks][inner] fp32 (each a positive normal power of two)
+ *   w  [outer][ceil(kblocks/4)][inner] uint32
+ * orc_ue8m0_encode(s) = log2(s) + 127 for such an s; orc_ue8m0_decode(e) =
+ * 2^(e - 127).  Unpacking writes the decoded fp32 scales back. */
+uint8_t orc_ue8m0_encode(float s);
+double orc_ue8m0_decode(uint8_t e);
+void orc_pack_ue8m0(const float *sf, int outer, int kblocks, int inner, uint32_t *w);
+void orc_unpack_ue8m0(const uint32_t *w, int outer, int kblocks, int inner, float *sf);
+
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int orc_num_threads(void);
 void orc_set_num_threads(int n);

@@ -86,6 +86,30 @@ int main() {
     EXPECT_NO_DEVICE(dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0(P, PF, P, PF, PI, nullptr, PFw, 64, 64, 256, 2,
                                                                nullptr));
 
+    // packed power-of-two scales and their packer
+    const uint32_t *PW = reinterpret_cast<const uint32_t *>(P);
+    uint32_t *PWw = reinterpret_cast<uint32_t *>(P);
+    EXPECT(dg_fp8_gemm_nt_ue8m0_packed(P, nullptr, 64, P, PW, nullptr, PHw, 64, 64, 128, nullptr, 0, nullptr),
+           DG_ERR_NULL);
+    EXPECT(dg_fp8_gemm_nt_ue8m0_packed(P, PW, 60, P, PW, nullptr, PHw, 64, 64, 128, nullptr, 0, nullptr),
+           DG_ERR_ALIGN);
+    EXPECT(dg_fp8_gemm_nt_ue8m0_packed(P, PW, 1 << 20, P, PW, nullptr, PHw, 1 << 20, 64, 4096, nullptr, 0, nullptr),
+           DG_ERR_SHAPE);
+    EXPECT_NO_DEVICE(dg_fp8_gemm_nt_ue8m0_packed(P, PW, 64, P, PW, nullptr, PHw, 64, 2112, 640, P, 1 << 20, nullptr));
+    EXPECT(dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed(P, PW, P, PW, nullptr, PHw, PI, 200, 64, 128, 2, nullptr),
+           DG_ERR_SHAPE);
+    EXPECT_NO_DEVICE(dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed(P, PW, P, PW, nullptr, PHw, PI, 256, 64, 384,
+                                                                      2, nullptr));
+    EXPECT(dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed(P, PW, P, PW, nullptr, PHw, nullptr, 2, 256, 64, 128, 64,
+                                                        nullptr),
+           DG_ERR_NULL);
+    EXPECT_NO_DEVICE(dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed(P, PW, P, PW, nullptr, PHw, PI, 2, 256, 64, 1152,
+                                                                  64, nullptr));
+    EXPECT(dg_pack_sf_ue8m0(PF, 0, 4, 8, PWw, nullptr), DG_ERR_SHAPE);
+    EXPECT(dg_pack_sf_ue8m0(PF, 1, 4, 8, reinterpret_cast<uint32_t *>(P + 2), nullptr), DG_ERR_ALIGN);
+    EXPECT(dg_pack_sf_ue8m0(PF, 1 << 30, 4, 1 << 30, PWw, nullptr), DG_ERR_SHAPE);
+    EXPECT_NO_DEVICE(dg_pack_sf_ue8m0(PF, 1, 5, 64, PWw, nullptr));
+
     // quantisers
     EXPECT(dg_quantize_e4m3_1x128(PF, 1, 64, 100, P, PFw, 64, nullptr), DG_ERR_SHAPE);
     EXPECT(dg_quantize_e4m3_1x128(PF, 1, 64, 128, P, PFw, 62, nullptr), DG_ERR_ALIGN);

@@ -25,6 +25,7 @@ hipError_t launch_gemm(const GemmProblem &, int, hipStream_t, std::string &confi
     config = "stub";
     return hipErrorInvalidValue;
 }
+hipError_t launch_pack_ue8m0(const float *, int, int, int, uint32_t *, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t noalloc_scratch(hipStream_t, void **, size_t *) { return hipErrorInvalidValue; }
 
 }  // namespace dg

@@ -234,3 +234,25 @@ def test_ue8m0_layout_and_k_grouped_argument_errors(lib):
     f = lib.dg_k_grouped_fp8_gemm_tn_contiguous_ue8m0
     assert f(P, P, P, P, NULL, NULL, P, 64, 64, 128, 2, S) == -1
     assert f(P, P, P, P, P, NULL, P, 64, 40, 128, 2, S) == -3
+
+
+def test_packed_ue8m0_argument_errors(lib):
+    f = lib.dg_fp8_gemm_nt_ue8m0_packed
+    assert f(NULL, P, 64, P, P, NULL, P, 64, 64, 128, NULL, 0, S) == -1
+    assert f(P, P, 64, P, P, NULL, P, 64, 64, 200, NULL, 0, S) == -2
+    assert f(P, P, 60, P, P, NULL, P, 64, 64, 128, NULL, 0, S) == -3       # ld_sfa < M
+    assert f(P, MIS, 64, P, P, NULL, P, 64, 64, 128, NULL, 0, S) == -3
+    assert f(P, P, 1 << 20, P, P, NULL, P, 1 << 20, 64, 1 << 12, NULL, 0, S) == -2   # K * M >= 2^31
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0_packed
+    assert f(P, P, P, P, NULL, P, NULL, 256, 64, 128, 2, S) == -1
+    assert f(P, P, P, P, NULL, P, P, 200, 64, 128, 2, S) == -2
+    assert f(P, P, P, P, NULL, P, P, 256, 1 << 20, 1 << 12, 2, S) == -2    # K * N >= 2^31
+    f = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0_packed
+    assert f(P, P, P, P, NULL, P, NULL, 2, 64, 64, 128, 0, S) == -1
+    assert f(P, P, P, P, NULL, P, P, 0, 64, 64, 128, 0, S) == -2
+    assert f(P, P, P, P, NULL, MIS, P, 2, 64, 64, 128, 0, S) == -3
+    f = lib.dg_pack_sf_ue8m0
+    assert f(NULL, 1, 4, 8, P, S) == -1
+    assert f(P, 1, 0, 8, P, S) == -2
+    assert f(P, 1, 4, 8, ct.c_void_p(0x10002), S) == -3
+    assert f(P, 1 << 30, 4, 1 << 30, P, S) == -2                          # too many workgroups

@@ -282,6 +282,65 @@ def test_quantize_ue8m0_codes_are_the_e4m3_rounding_of_x_times_two_to_minus_e(ki
     assert np.array_equal(q, ref)
 
 
+def _packed_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "ue8m0_packed_words.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                o, q, w0, w1 = line.split()
+                rows.append((int(o), int(q), int(w0, 16), int(w1, 16)))
+    words = np.zeros((2, 2, 2), dtype=np.uint32)
+    for o, q, w0, w1 in rows:
+        words[o, q] = (w0, w1)
+    log2 = np.array([[[0, -3], [1, 5], [-1, 0], [-10, 12], [2, -126]],
+                     [[127, 7], [-126, 7], [3, 7], [4, 7], [-20, 0]]], dtype=np.int32)   # [o][kb][i]
+    return np.ldexp(np.float32(1.0), log2).astype(np.float32), words
+
+
+def test_ue8m0_pack_matches_hand_worked_words():
+    """Packing the hand-worked example of tests/golden/ue8m0_packed_words.txt
+    (four K blocks per word, block 4q + j in byte j, zero high bytes in the
+    last word) gives exactly the words derived there, and unpacking them
+    returns the scales."""
+    sf, words = _packed_golden()
+    got = oracle.pack_ue8m0(sf, k_axis=1)
+    assert got.shape == (2, 2, 2) and got.dtype == np.uint32
+    assert np.array_equal(got, words), [hex(v) for v in got.reshape(-1)]
+    assert np.array_equal(oracle.unpack_ue8m0(words, 5, k_axis=1), sf)
+
+
+def test_ue8m0_code_is_the_ieee_exponent_field_of_every_normal_power_of_two():
+    """A UE8M0 code (bias 127) of 2^k is the biased exponent field of the
+    IEEE-754 single 2^k, read here from the bit pattern (a route that shares
+    nothing with the oracle's frexp); decoding returns 2^k exactly."""
+    for k in range(-126, 128):
+        s = np.float32(np.ldexp(1.0, k))
+        field = int(np.array([s], dtype=np.float32).view(np.uint32)[0] >> 23) & 0xFF
+        assert oracle.ue8m0_encode(s) == field == k + 127
+        assert oracle.ue8m0_decode(k + 127) == 2.0 ** k
+
+
+@pytest.mark.parametrize("K", [128, 384, 512, 640, 1152])
+def test_ue8m0_pack_round_trips_quantiser_scales_in_both_layouts(K):
+    """The power-of-two quantisers' scales survive pack -> unpack in the
+    layouts the GEMMs take them in (sfa [K/128][ld] packed along its first
+    axis, sfb [G][N/128][K/128] along its last), for K-block counts that do
+    and do not fill the last word (whose unused high bytes stay zero)."""
+    x = synth.normal_f32(31, 0, (70, K)) * np.ldexp(np.float32(1.0), synth.randint(31, 1, 70 * K, -30, 30).reshape(70, K)).astype(np.float32)
+    _, sfa = oracle.quantize_1x128(x, ue8m0=True)
+    xb = synth.normal_f32(31, 2, (2, 200, K))
+    _, sfb = oracle.quantize_128x128(xb, ue8m0=True)
+    nkb = K // 128
+    pa = oracle.pack_ue8m0(sfa[:, :70].copy(), k_axis=0)
+    assert pa.shape == ((nkb + 3) // 4, 70)
+    assert np.array_equal(oracle.unpack_ue8m0(pa, nkb, k_axis=0), sfa[:, :70])
+    pb = oracle.pack_ue8m0(sfb, k_axis=-1)
+    assert pb.shape == (2, 2, (nkb + 3) // 4)
+    assert np.array_equal(oracle.unpack_ue8m0(pb, nkb, k_axis=-1), sfb)
+    if nkb % 4:
+        assert np.all(pb[..., -1] >> (8 * (nkb % 4)) == 0)
+
+
 def test_quantize_ue8m0_equals_plain_when_scales_are_powers_of_two():
     """Blocks whose amax is 448 times a power of two have a power-of-two
     plain scale already: both quantisers give the same codes and scales."""
