@@ -15,34 +15,44 @@
 // exponent-scaled FP8 MFMA; dividing by it is exact.
 //
 // Both kernels are HBM-bound: 4 bytes read and 1 byte written per element.
+// Per element they do a handful of vector instructions: the quotient through
+// an fp64 reciprocal per block (exact, see div_by_scale) and the hardware
+// fp8 conversion (bit-exact in the range the quotients take).
 #include "dg_device.h"
 #include "dg_internal.h"
 
 namespace dg {
 
-// Round |v| (finite, < 448) to the E4M3FN grid, nearest with ties to even.
-// Normal range [2^-6, 448): keep 3 of the 23 fp32 mantissa bits with an
-// integer round-half-even on the dropped 20 bits (a carry moves into the
-// exponent, as it should).  Subnormal range [0, 2^-6): the grid step is 2^-9,
-// so the code is rint(|v| * 2^9) (exact scaling, rint ties to even), and 8
-// becomes code 0x08 = 2^-6, the smallest normal.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t mag = u & 0x7fffffffu;
-    if (mag > 0x7f800000u) return 0x7fu;                  // NaN
-    const float a = __uint_as_float(mag);
-    uint32_t code;
-    if (a >= 448.0f) {
-        code = 0x7eu;                                      // saturate (also +-inf)
-    } else if (a < 0.015625f) {                            // 2^-6
-        code = (uint32_t)__builtin_rintf(a * 512.0f);
-    } else {
-        const uint32_t r = mag + 0x7ffffu + ((mag >> 20) & 1u);
-        const uint32_t e = (r >> 23) - 127u + 7u;          // biased E4M3 exponent, 1..15
-        code = (e << 3) | ((r >> 20) & 7u);
-    }
-    return sign | code;
+// Four quotients x / s, already rounded to fp32, to E4M3FN codes (byte i
+// from element i) with gfx950's packed conversion.  For every finite |v| <
+// 464 it gives the nearest E4M3FN value, ties to the even code, subnormals
+// (steps of 2^-9 below 2^-6) included, which was checked against a software
+// encoder over all 2^32 fp32 inputs.  Above 464 it does not saturate, but a
+// block's values divided by its scale stay below 448 * (1 + 2^-23).  NaN keeps
+// its sign through the conversion; NaN codes are made positive (0x7f) here,
+// the quantisers' NaN code.
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    const uint32_t u = (uint32_t)w;
+    const uint32_t nan = ((u & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;   // bytes whose low 7 bits are all ones
+    return u & ~nan;
+}
+
+// x / s rounded to fp32 (IEEE division), for finite s > 0, from y = 1/s
+// rounded to fp64: RN32(x * y) with the product rounded to fp64 first.  This
+// is exact: a quotient of two fp32 values is never closer than 2^-49
+// (relative) to a point halfway between two fp32 values, while the two fp64
+// roundings move it by less than 2^-51, so both round to the same fp32.
+// (x = +-inf or NaN gives NaN, as the division does; s = inf gives y = 0.)
+__device__ __forceinline__ float div_by_scale(float x, double y) { return (float)((double)x * y); }
+
+// The block's four quotients as codes.  Power-of-two scales: multiplying by
+// the exact reciprocal is the division.
+template <bool UE8M0>
+__device__ __forceinline__ uint32_t encode_block4(const v4f &v, float inv, double y) {
+    if constexpr (UE8M0) return e4m3_encode4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    return e4m3_encode4(div_by_scale(v.x, y), div_by_scale(v.y, y), div_by_scale(v.z, y), div_by_scale(v.w, y));
 }
 
 template <bool UE8M0>
@@ -55,28 +65,33 @@ __device__ __forceinline__ float block_scale(float amax) {
     return __uint_as_float((u & 0x7fffffu) ? (u & 0x7f800000u) + 0x00800000u : u);
 }
 
-// 1x128: a half-wave (32 lanes x float4) per 128-element block.  A
-// workgroup of 8 half-waves takes 8 consecutive rows (of all groups, flat)
-// and U consecutive K blocks of each: every half-wave issues the loads of
-// its U blocks (one contiguous run of U*512 bytes) before any arithmetic, so
-// U*16 bytes per lane are in flight, and for each K block the 8 scales of the
-// workgroup land in 32 consecutive bytes of the transposed layout.  x is read
-// once: nontemporal loads keep it out of the caches that the codes (read
-// next by the GEMM) live in.
+// 1x128: eight lanes per 128-element block; lane j of the eight holds the
+// 16-byte chunks j, j+8, j+16 and j+24 of the block, so that every load
+// instruction reads whole 128-byte rows of it.  Wave w of a workgroup takes
+// 8 consecutive rows (of all groups, flat; lanes 8i .. 8i+7 take row i) and U
+// consecutive K blocks, the four waves consecutive runs of U blocks; a wave
+// issues all its loads before any arithmetic.  Per K block the 8 scales of a
+// wave land in 32 consecutive bytes of the transposed layout, and the
+// per-block work (reduction, scale, reciprocals) is spread over 16 values per
+// lane.  x is read once: nontemporal loads keep it out of the caches that
+// the codes (read next by the GEMM) live in.
 template <bool UE8M0, int U>
 __global__ void __launch_bounds__(256)
 quant_1x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ sf,
                    int rows, int nkb, int ld_sf, int64_t rows_total, int kb_tiles) {
-    const int64_t row_all = (int64_t)(blockIdx.x / kb_tiles) * 8 + (threadIdx.x >> 5);
-    const int kb0 = (int)(blockIdx.x % kb_tiles) * U;
-    const int l = threadIdx.x & 31;
-    if (row_all >= rows_total) return;
-    const float *xr = x + row_all * nkb * kKBlock;
-    v4f v[U];
+    const int lane = threadIdx.x & 63;
+    const int64_t row_all = (int64_t)(blockIdx.x / kb_tiles) * 8 + (lane >> 3);
+    const int kb0 = ((int)(blockIdx.x % kb_tiles) * 4 + (int)(threadIdx.x >> 6)) * U;
+    const int j = lane & 7;
+    if (row_all >= rows_total || kb0 >= nkb) return;
+    const v4f *xr = reinterpret_cast<const v4f *>(x + row_all * nkb * kKBlock);
+    v4f v[U][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (kb0 + u < nkb)
-            v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + (int64_t)(kb0 + u) * kKBlock) + l);
+        if (kb0 + u < nkb) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[u][c] = __builtin_nontemporal_load(xr + (int64_t)(kb0 + u) * 32 + j + 8 * c);
+        }
     }
     const int64_t g = row_all / rows;
     const int r = (int)(row_all - g * rows);
@@ -84,14 +99,19 @@ quant_1x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float *
     for (int u = 0; u < U; ++u) {
         const int kb = kb0 + u;
         if (kb >= nkb) break;
-        float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+        float amax = 0.0f;
 #pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+        for (int c = 0; c < 4; ++c)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][c].x), fabsf(v[u][c].y)), fmaxf(fabsf(v[u][c].z), fabsf(v[u][c].w))));
+#pragma unroll
+        for (int o = 4; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 8));
         const float s = block_scale<UE8M0>(amax);
-        const uint32_t packed = e4m3_encode(v[u].x / s) | (e4m3_encode(v[u].y / s) << 8) |
-                                (e4m3_encode(v[u].z / s) << 16) | (e4m3_encode(v[u].w / s) << 24);
-        reinterpret_cast<uint32_t *>(q + (row_all * nkb + kb) * kKBlock)[l] = packed;
-        if (l == 0) sf[(g * nkb + kb) * (int64_t)ld_sf + r] = s;
+        const float inv = 1.0f / s;
+        const double y = 1.0 / (double)s;
+        uint32_t *qb = reinterpret_cast<uint32_t *>(q + (row_all * nkb + kb) * kKBlock);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qb[j + 8 * c] = encode_block4<UE8M0>(v[u][c], inv, y);
+        if (j == 0) sf[(g * nkb + kb) * (int64_t)ld_sf + r] = s;
     }
 }
 
@@ -126,13 +146,14 @@ quant_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q, float
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = block_scale<UE8M0>(amax);
+    const float inv = 1.0f / s;
+    const double y = 1.0 / (double)s;
     uint8_t *qg = q + g * rows * (int64_t)K;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int r = r0 + (t >> 5) + 8 * i;
         if (r < rows) {
-            const uint32_t packed = e4m3_encode(v[i].x / s) | (e4m3_encode(v[i].y / s) << 8) |
-                                    (e4m3_encode(v[i].z / s) << 16) | (e4m3_encode(v[i].w / s) << 24);
+            const uint32_t packed = encode_block4<UE8M0>(v4f{v[i].x, v[i].y, v[i].z, v[i].w}, inv, y);
             *reinterpret_cast<uint32_t *>(qg + (int64_t)r * K + col) = packed;
         }
     }
@@ -171,7 +192,7 @@ template <int U>
 static hipError_t launch_quant_1x128_u(const float *x, int groups, int rows, int nkb, uint8_t *q, float *sf,
                                        int ld_sf, hipStream_t stream, bool ue8m0) {
     const int64_t rows_total = (int64_t)groups * rows;
-    const int kb_tiles = (nkb + U - 1) / U;
+    const int kb_tiles = (nkb + 4 * U - 1) / (4 * U);        // runs of 4U K blocks per workgroup
     const int64_t grid = (rows_total + 7) / 8 * kb_tiles;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (ue8m0)
@@ -186,12 +207,10 @@ static hipError_t launch_quant_1x128_u(const float *x, int groups, int rows, int
 hipError_t launch_quant_1x128(const float *x, int groups, int rows, int K, uint8_t *q, float *sf,
                               int ld_sf, hipStream_t stream, bool ue8m0) {
     const int nkb = K / kKBlock;
-    // four blocks per half-wave when that still leaves a few workgroups per
-    // CU; fewer for small (decode) inputs, so that more CUs take a share
+    // two blocks per wave when that still leaves a few workgroups per CU;
+    // one for small (decode) inputs, so that more CUs take a share
     const int64_t row_groups = ((int64_t)groups * rows + 7) / 8;
-    if (row_groups * ((nkb + 3) / 4) >= 2048)
-        return launch_quant_1x128_u<4>(x, groups, rows, nkb, q, sf, ld_sf, stream, ue8m0);
-    if (row_groups * ((nkb + 1) / 2) >= 1024)
+    if (row_groups * ((nkb + 7) / 8) >= 1024)
         return launch_quant_1x128_u<2>(x, groups, rows, nkb, q, sf, ld_sf, stream, ue8m0);
     return launch_quant_1x128_u<1>(x, groups, rows, nkb, q, sf, ld_sf, stream, ue8m0);
 }
