@@ -36,7 +36,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["dg_device.h", "dg_internal.h", "dg_pipeline.h", "gemm.hip", "decode.hip", "pipelined.hip", "mqa.hip",
-                  "persistent.hip", "quant.hip"]
+                  "persistent.hip", "quant.hip", "stream.hip", "noalloc.hip"]
 
 
 def kernel_source_hash():
