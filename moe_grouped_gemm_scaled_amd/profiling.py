@@ -167,6 +167,9 @@ def _kernel_fragment(config):
         bm, bn = kv["tile"].split("x")[:2]
         wm, wn = kv["waves"].split("x")
         frag = f"{fam}_kernel<{bm}, {bn}, {wm}, {wn}, {kv['stages']}, {kv['kblocks_per_stage']}, "
+    elif fam == "stream":
+        wm, wn = kv["waves"].split("x")
+        frag = f"stream_kernel<{int(kv['rows']) // 16}, {int(kv['cols']) // 16}, {wm}, {wn}, {kv['stages']}>"
     elif fam == "mqa":
         frag = f"mqa_kernel<{int(kv['heads']) // 16}, "
     elif fam == "skinny":

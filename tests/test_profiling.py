@@ -81,3 +81,14 @@ def test_mfma_summary(tmp_path):
 def test_kernel_fragment_matches_pipe_symbol():
     frag, grid = profiling._kernel_fragment(CONFIG)
     assert frag in KERNEL and grid == 448
+
+
+def test_kernel_fragment_matches_stream_and_skinny_symbols():
+    frag, grid = profiling._kernel_fragment("family=stream rows=64 cols=32 waves=4x1 stages=8 splits=3+ grid=256")
+    assert grid == 256 and "void dg::stream_kernel<4, 2, 4, 1, 8>(dg::StreamParams)".find(frag) > 0
+    frag, grid = profiling._kernel_fragment("family=stream rows=128 cols=128 waves=2x4 stages=4 splits=4+ grid=256")
+    assert "void dg::stream_kernel<8, 8, 2, 4, 4>(dg::StreamParams)".find(frag) > 0
+    assert "void dg::stream_kernel<8, 8, 2, 4, 5>(dg::StreamParams)".find(frag) < 0
+    frag, grid = profiling._kernel_fragment(
+        "family=skinny mode=0 rows=64 cols=96 waves=4x3 ks=1 pd=2 splits=1 grid=256")
+    assert "void dg::skinny_kernel<4, 6, 4, 3, 1, 2, (dg::Mode)0>(dg::SkinnyParams)".find(frag) > 0
