@@ -445,7 +445,7 @@ int dg_get_num_cus(void);
 
 /* Kernel family used by the GEMM entry points called from this thread, for
  * tuning and testing: "auto" (the default: chosen per problem), "pipe",
- * "persist", "skinny" or "tiled".  Not on the pages (whose JIT picks one
+ * "persist", "skinny", "stream" or "tiled".  Not on the pages (whose JIT picks one
  * kernel per shape, "Utilities and environment variables"); here every
  * family stays reachable so each can be tested.  A family that cannot take a
  * problem falls back to the automatic choice; results agree to the
