@@ -12,6 +12,11 @@ namespace dg {
 
 #define DG_LDS(ptr) ((__attribute__((address_space(3))) void *)(ptr))
 
+// A buffer-load offset past the end of any buffer this library describes
+// (their ranges stay below 2^31): the load returns zeros and moves no data.
+// Used for loads that exist only to keep every wave's load count equal.
+constexpr int kOutOfRange = 0x7ffffff0;
+
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone, n < 64
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 

@@ -149,12 +149,14 @@ pipe_kernel(PipeParams p) {
     constexpr int NBW = BN >= 128 ? BN / 128 : 1; // 128-wide scale blocks under the tile's columns
     // stage layout: KS K blocks of A (BM x 128 B each), KS of B, then per K
     // block kk a 1-KB slot of A scales (sfa[kb+kk][m0 + 4l .. +3] at 16 l),
-    // then 1 KB of B scales (sfb[n0/128 + l][kb .. kb+3] at 16 l)
+    // then 1 KB of B scales (sfb[n0/128 + l][kb .. kb+3] at 16 l), then 1 KB
+    // where the scale loads of the waves that fetch none land (zeros)
     constexpr int BLK_A = BM * kKBlock, BLK_B = BN * kKBlock;
     constexpr int OFF_B = KS * BLK_A;
     constexpr int OFF_SA = OFF_B + KS * BLK_B;
     constexpr int OFF_SB = OFF_SA + KS * 1024;
-    constexpr int STAGE = OFF_SB + 1024;
+    constexpr int OFF_JUNK = OFF_SB + 1024;
+    constexpr int STAGE = OFF_JUNK + 1024;
     constexpr int DA = KS * BM / (8 * NW), DB = KS * BN / (8 * NW);   // 1-KB LDS-DMA chunks per wave per step
     constexpr int PER_BLOCK = DA + DB + 1;        // loads per wave per step
     static_assert(KS == 1 || KS == 2 || KS == 4, "K blocks per stage");
@@ -350,24 +352,29 @@ pipe_kernel(PipeParams p) {
     const int lds_a = wk * BLK_A + wr * 1024;
     const int lds_b = OFF_B + wk * BLK_B + wr * 1024;
     // scales: lane l of wave w < KS fetches sfa[kb + w][m0 + 4l .. +3] (16 B);
-    // lane l of every other wave the 16 B starting at sfb[n0/128 + l][kb]
-    // (the scales of K blocks kb .. kb+3; all of these waves write the same
-    // bytes).  Lanes past the tile fetch harmless in-range or zero-filled data
-    // into unused slots.
-    // K-grouped: B scales are per column (sfb[kb][n]); lane l of a B-scale
-    // wave fetches sfb[kb][n0 + 4l .. +3] (clamped to the last 4 columns).
+    // lane l < NBW of wave KS the 16 B starting at sfb[n0/128 + l][kb] (the
+    // scales of K blocks kb .. kb+3).  Every other lane, and every lane of the
+    // other waves (whose load lands in a junk slot), points out of range:
+    // zeros, no memory traffic, and every wave still issues one scale load
+    // per step (measured: fetching the same B scales from every wave and lane
+    // cost about 7 us of DMA time at M = N = 4096, K = 7168).
+    // K-grouped: B scales are per column (sfb[kb][n]); lane l of wave KS
+    // fetches sfb[kb][n0 + 4l .. +3] (clamped to the last 4 columns).
     // Packed scales (PK): wave w < KS fetches the words of K block kb + w
     // (row (kb + w)/4 of the packed sfa), B-scale waves the 4 words from
     // (kb/4) of their scale row: K blocks 4(kb/4) .. +15, which hold every K
     // block of the step.
     const bool wsa = wave < KS;
+    const bool wsb = wave == KS;
     const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
         wsa ? (void *)SFA : (void *)SFB, (short)0, wsa ? nkw * ld * 4 : (KG ? nkb * N * 4 : nnb * nkw * 4),
         0x00020000);
     const int sa_row = m0 + 4 * lane;
     const int v_s = wsa ? ((sa_row < ld ? sa_row : 0) + (PK ? 0 : wave * ld)) * 4
-                        : (KG ? min(n0 + 4 * lane, N - 4) * 4 : min(n0 / 128 + lane, nnb - 1) * nkw * 4);
-    const int lds_s = wsa ? OFF_SA + wave * 1024 : OFF_SB;
+                  : !wsb ? kOutOfRange
+                  : KG ? min(n0 + 4 * lane, N - 4) * 4
+                  : lane < NBW ? min(n0 / 128 + lane, nnb - 1) * nkw * 4 : kOutOfRange;
+    const int lds_s = wsa ? OFF_SA + wave * 1024 : (wsb ? OFF_SB : OFF_JUNK);
     const int s_stride = wsa ? ld * 4 : (KG ? N * 4 : 4);
 
     // DMA of step st (K blocks KS*st .. +KS-1) into stage stg

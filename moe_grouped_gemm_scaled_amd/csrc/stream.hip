@@ -146,7 +146,6 @@ stream_kernel(StreamParams p) {
     const int dchunk = ((lane & 7) ^ (lane >> 3)) * 16;
     // A pad load (q >= NL) points past the end of A: the range check turns it
     // into zeros written to the pad area, with no memory traffic
-    constexpr int kOutOfRange = 0x7ffffff0;
     int vq[DPW];
     static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
