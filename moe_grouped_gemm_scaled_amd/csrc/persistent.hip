@@ -78,7 +78,8 @@ persist_kernel(PersistParams p) {
     constexpr int OFF_B = KS * BLK_A;
     constexpr int OFF_SA = OFF_B + KS * BLK_B;
     constexpr int OFF_SB = OFF_SA + KS * 1024;
-    constexpr int STAGE = OFF_SB + 1024;
+    constexpr int OFF_JUNK = OFF_SB + 1024;       // scale loads of the waves that fetch none (zeros)
+    constexpr int STAGE = OFF_JUNK + 1024;
     constexpr int DA = KS * BM / (8 * NW), DB = KS * BN / (8 * NW);
     constexpr int PER_STEP = DA + DB + 1;
     constexpr int EPI_ROWS = 16;                  // epilogue chunk rows per wave
@@ -214,7 +215,8 @@ persist_kernel(PersistParams p) {
     const int lds_a = wk * BLK_A + wr * 1024;
     const int lds_b = OFF_B + wk * BLK_B + wr * 1024;
     const bool wsa = wave < KS;
-    const int lds_s = wsa ? OFF_SA + wave * 1024 : OFF_SB;
+    const bool wsb = wave == KS;
+    const int lds_s = wsa ? OFF_SA + wave * 1024 : (wsb ? OFF_SB : OFF_JUNK);
     const int s_stride = wsa ? ld * 4 : 4;
     // Lane offsets are the same for every tile (row within the tile, chunk);
     // the tile's position is in the buffer descriptors: base at the tile's
@@ -230,9 +232,11 @@ persist_kernel(PersistParams p) {
         constexpr int i = decltype(ic)::value;
         vb[i] = (8 * (wr + RG_STEP * i) + (lane >> 3)) * K + wk * kKBlock + dchunk;
     });
-    // scales: lane l of wave w < KS fetches sfa[kb + w][m0 + 4l .. +3]; lane l
-    // of the other waves the 16 B at sfb[n0/128 + l][kb]
-    const int v_s = wsa ? (4 * lane + wave * ld) * 4 : lane * nkb * 4;
+    // scales: lane l of wave w < KS fetches sfa[kb + w][m0 + 4l .. +3]; lane
+    // l < NBW of wave KS the 16 B at sfb[n0/128 + l][kb].  The other lanes and
+    // waves point out of range (zeros into unused or junk slots, no memory
+    // traffic), so that every wave issues one scale load per step.
+    const int v_s = wsa ? (4 * lane + wave * ld) * 4 : (wsb && lane < NBW ? lane * nkb * 4 : kOutOfRange);
     __amdgpu_buffer_rsrc_t rA, rB, rS;
     // Masked: each tile walks its K steps from a hashed start (wrapping
     // round), the same for every row tile of a (group, column tile), so that
