@@ -382,9 +382,9 @@ static hipError_t launch_stream_t(const GemmProblem &p, int units, hipStream_t s
 
 // Configuration per shape: 96-column tiles where they leave fewer columns per
 // CU than 128-column ones and already cover the CUs, 32-column tiles for
-// narrow N, 128 otherwise (64 and 32 measured slower at N = 7168,
-// K = 16384); K split over about one workgroup per CU when the tiles leave
-// CUs idle.
+// narrow N, 112 or 128 otherwise, whichever gives the busiest workgroup
+// fewer bytes (64 and 32 measured slower at N = 7168, K = 16384); K split
+// over about one workgroup per CU when the tiles leave CUs idle.
 hipError_t launch_stream(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config) {
     if (!stream_eligible(p)) return hipErrorInvalidValue;
     const int cus = num_cus > 0 ? num_cus : 256;
@@ -404,6 +404,22 @@ hipError_t launch_stream(const GemmProblem &p, int num_cus, hipStream_t stream, 
     if (w96) {
         if (small_m) return launch_stream_t<4, 6, 1, 6, 5>(p, cus, stream, config);
         return launch_stream_t<8, 6, 2, 3, 4>(p, cus, stream, config);
+    }
+    // 112-column tiles (seven waves of 16 columns) where they give the
+    // busiest workgroup fewer bytes of B than 128-column ones: at N = 7168,
+    // K = 16384, 64 tiles of 4 equal splits against 56 tiles of 4 or 5, 29.1
+    // against 31.6 us at M = 64 and 34.9 against 39.0 us at M = 128 (MI355X)
+    const int nkb = p.K / kKBlock;
+    auto busiest = [&](int w) -> int64_t {        // columns x K blocks of the busiest workgroup
+        const int64_t t = (p.N + w - 1) / w;
+        if (t >= cus) return (t + cus - 1) / cus * w * (int64_t)nkb;
+        int64_t lo = cus / t;
+        if (lo > nkb / 2) lo = nkb / 2 > 0 ? nkb / 2 : 1;
+        return w * ((nkb + lo - 1) / lo);
+    };
+    if (busiest(112) < busiest(128)) {
+        if (small_m) return launch_stream_t<4, 7, 1, 7, 4>(p, cus, stream, config);
+        return launch_stream_t<8, 7, 1, 7, 3>(p, cus, stream, config);
     }
     if (small_m) return launch_stream_t<4, 8, 1, 8, 5>(p, cus, stream, config);
     return launch_stream_t<8, 8, 2, 4, 4>(p, cus, stream, config);

@@ -1,8 +1,9 @@
-"""GPU parity of the streaming decode family (B loaded straight into a
-per-wave register ring, A through an LDS ring, optional split-K) against the
-CPU oracle: every tile configuration it takes (64-, 96- and 128-column tiles,
-up to 64 and up to 128 rows), M and N tails, one-block and odd K, K ranges
-longer than one unrolled chunk, with and without C, and C aliasing D.
+"""GPU parity of the streaming decode family (all rows of A and a column
+tile of B per workgroup, one K block per LDS stage filled by DMA, optional
+split-K) against the CPU oracle: every tile configuration it takes (32-, 96-,
+112- and 128-column tiles, up to 64 and up to 128 rows), M and N tails,
+one-block and odd K, K ranges longer than one unrolled chunk, with and
+without C, and C aliasing D.
 Bar: |D - D_ref| <= ulp_bf16(D_ref) + 1e-4 max|D_ref|, every element.
 """
 import sys
@@ -65,6 +66,16 @@ SHAPES = [(64, 2112, 2048, False), (128, 2112, 1792, True), (1, 300, 384, False)
 def test_stream_shapes(M, N, K, with_c):
     announce(f"stream {M}x{N}x{K} C={with_c}")
     run(M, N, K, with_c, seed=M * 7 + N + K)
+
+
+@pytest.mark.parametrize("M,N,K,with_c", [(40, 7000, 4096, True), (128, 7000, 2048, False), (64, 7168, 1536, False)])
+def test_stream_112_column_tiles(M, N, K, with_c):
+    """Shapes where 112-column tiles give the busiest workgroup fewer bytes
+    than 128-column ones (N = 7000 leaves a partial last tile, and tiles
+    start inside 128-wide scale blocks)."""
+    announce(f"stream 112 {M}x{N}x{K} C={with_c}")
+    cfg = run(M, N, K, with_c, seed=M + N + K + 11)
+    assert "cols=112" in cfg, cfg
 
 
 def test_stream_c_aliases_d():
