@@ -397,9 +397,11 @@ hipError_t launch_stream(const GemmProblem &p, int num_cus, hipStream_t stream, 
     if (p.N < 4096) {
         // 32-column tiles: about four splits per tile, so the last split reads
         // few partials (measured on MI355X, N = 2112, K = 7168: 10.6 against
-        // 13.6 us with 64-column tiles at M = 64, 14.1 against 17.2 at M = 128)
-        if (small_m) return launch_stream_t<4, 2, 4, 1, 8>(p, cus, stream, config);
-        return launch_stream_t<8, 2, 8, 1, 5>(p, cus, stream, config);
+        // 13.6 us with 64-column tiles at M = 64, 14.1 against 17.2 at M = 128;
+        // 48-column tiles 12.2 and 17.3 us).  Stages: 5 and 4 (10.2 against
+        // 10.8 us with 8 at M = 64; 14.0 against 14.2 us with 5 at M = 128)
+        if (small_m) return launch_stream_t<4, 2, 4, 1, 5>(p, cus, stream, config);
+        return launch_stream_t<8, 2, 8, 1, 4>(p, cus, stream, config);
     }
     if (w96) {
         if (small_m) return launch_stream_t<4, 6, 1, 6, 5>(p, cus, stream, config);
