@@ -122,6 +122,8 @@ float orc_block_scale_ue8m0(float amax)
 {
     const float s = orc_block_scale(amax);
     int e;
+    if (isinf(s))
+        return s;                           /* a block holding +-inf: no power of two above it */
     const float m = frexpf(s, &e);
     return m == 0.5f ? s : ldexpf(1.0f, e);
 }

@@ -766,3 +766,18 @@ def test_k_grouped_split_group_sums_and_sampled_form():
     ns = np.array([47, 0, 20, 9], np.int32)
     at = oracle.k_grouped_tn_at(a, sfa, b, sfb, np.array([128, 256], np.int32), None, gs, ms, ns)
     assert np.array_equal(at, parts[gs, ms, ns])
+
+
+def test_block_scales_of_an_infinite_block_stay_infinite():
+    """A block holding +-inf has the IEEE quotient inf / 448 = inf as its
+    scale; there is no power of two above it, so the power-of-two form keeps
+    inf as well (its codes are then zeros of the values' signs, and 0x7f for
+    the infinities, inf / inf being NaN)."""
+    assert oracle.block_scale(np.float32(np.inf)) == np.inf
+    assert oracle.block_scale_ue8m0(np.float32(np.inf)) == np.inf
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0, :4] = [np.inf, -1.5, 2.0, -0.0]
+    for ue in (False, True):
+        q, sf = oracle.quantize_1x128(x, ue8m0=ue)
+        assert sf[0, 0] == np.inf
+        assert list(q[0, :4]) == [0x7F, 0x80, 0x00, 0x80]
