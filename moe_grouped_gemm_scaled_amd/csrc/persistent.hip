@@ -106,7 +106,7 @@ persist_kernel(PersistParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t stage3[NST > 3 ? STAGE : 16];
     __shared__ __attribute__((aligned(16))) uint8_t stage4[NST > 4 ? STAGE : 16];
     __shared__ __attribute__((aligned(16))) uint8_t stage5[NST > 5 ? STAGE : 16];
-    // the record {tile, step, flags, 0} of the step held by each stage, apart
+    // the record {tile, step, flags, valid rows} of the step held by each stage, apart
     // from the stages so that writing it never waits for a stage's DMA
     __shared__ v4i meta_sh[NST];
     __shared__ int row_list[LIST];
@@ -243,10 +243,13 @@ persist_kernel(PersistParams p) {
     // the workgroups streaming different weights spread over the DRAM
     // channels instead of all reading the same K offset of their rows.
     int p_rot = 0;
+    // rows of tile k that hold data: the rest read zeros (masked: rows at or
+    // past masked_m, neither fetched nor multiplied)
+    int p_valid = BM;
     // DMA descriptors of tile k (k < 0: tile 0 of group 0, for steps that are never multiplied)
     auto set_tile = [&](int k) __attribute__((always_inline)) {
-        int grp = 0, tm = 0, tn = 0;
-        if (k >= 0) tile_coords(k, grp, tm, tn);
+        int grp = 0, tm = 0, tn = 0, rt = 0;
+        if (k >= 0) tile_coords_rt(k, grp, tm, tn, rt);
         if constexpr (MODE == Mode::Masked && !STREAMK) p_rot = k_rotation(grp * p.tiles_n + tn, nsteps);
         const int m0 = tm * BM, n0 = tn * BN;
         const uint8_t *A = p.a;
@@ -261,8 +264,10 @@ persist_kernel(PersistParams p) {
             B += (int64_t)grp * N * K;
             SFB += (int64_t)grp * nnb * nkb;
         }
-        rA = __builtin_amdgcn_make_buffer_rsrc((void *)(A + (int64_t)m0 * K), (short)0, (rows_a - m0) * K,
-                                               0x00020000);
+        int arows = rows_a - m0;
+        if (MODE == Mode::Masked && k >= 0) arows = __builtin_amdgcn_readfirstlane((int)row_valid[rt]);
+        p_valid = arows < BM ? arows : BM;
+        rA = __builtin_amdgcn_make_buffer_rsrc((void *)(A + (int64_t)m0 * K), (short)0, arows * K, 0x00020000);
         rB = __builtin_amdgcn_make_buffer_rsrc((void *)(B + (int64_t)n0 * K), (short)0, (N - n0) * K, 0x00020000);
         if (wsa)
             rS = __builtin_amdgcn_make_buffer_rsrc((void *)(SFA + m0), (short)0, (nkb * ld - m0) * 4, 0x00020000);
@@ -645,16 +650,19 @@ persist_kernel(PersistParams p) {
             const v4i meta = meta_sh[(u + 1) % NST];
             const int c_k = __builtin_amdgcn_readfirstlane(meta.x);
             const int c_flags = __builtin_amdgcn_readfirstlane(meta.z);
+            const int c_valid = __builtin_amdgcn_readfirstlane(meta.w);
             if (c_flags & kMetaEnd) return false;
             const bool c_last = (c_flags & (kMetaCompute | kMetaLast)) == (kMetaCompute | kMetaLast);
             if (c_last) epi_prepare(c_k);
             uint8_t *dst = stage_of(sc);
             const int flags_p = producer_flags();
             dma(dst);
-            if (tid == 0) meta_sh[u] = v4i{p_k, p_s, flags_p, 0};
+            if (tid == 0) meta_sh[u] = v4i{p_k, p_s, flags_p, p_valid};
             advance();
             if (c_flags & kMetaCompute) {
-                compute(src);
+                // a wave whose rows all lie past the tile's data multiplies
+                // nothing: its sums stay zero and none of its rows is stored
+                if (wm * TM < c_valid) compute(src);
                 if (c_last) {
                     if (STREAMK && (c_flags & kMetaShareEnd)) {
                         end_k = c_k;
