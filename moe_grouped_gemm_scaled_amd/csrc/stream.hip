@@ -56,6 +56,15 @@ struct StreamParams {
     int splits_lo, split_hi, slots;
 };
 
+// Subtile rows per wave staged at once in the epilogue: the largest divisor
+// of SM whose WGM * CH * 16 rows of BN fp32 (plus a 4-float pad per row) fit
+// one stage.
+constexpr int epi_rows(int SM, int WGM, int BN, int STAGE) {
+    for (int c = SM; c >= 1; --c)
+        if (SM % c == 0 && WGM * c * 16 * (BN + 4) * 4 <= STAGE) return c;
+    return 0;
+}
+
 template <int MT, int NTN, int WGM, int WGN, int NST>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 stream_kernel(StreamParams p) {
@@ -79,6 +88,7 @@ stream_kernel(StreamParams p) {
     static_assert(NST >= 2 && NST <= 8 && NST * STAGE <= 160 * 1024, "stages fit the LDS");
     static_assert((NST - 2) * PER_BLOCK < 64, "vmcnt immediate");
     static_assert((ROWS + 3) / 4 <= 64 && (BN + 127) / 128 + 1 <= 64, "scale loads: one 16-byte slot per lane");
+    static_assert(epi_rows(MT / WGM, WGM, 16 * NTN, STAGE) > 0, "epilogue staging fits a stage");
 
     // one object per stage, so that the compiler can tell LDS reads of one
     // stage from DMA into another
@@ -282,43 +292,65 @@ stream_kernel(StreamParams p) {
         if (tid == 0) __hip_atomic_store(p.counters + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // ---- epilogue: D = bf16(acc + C); lane holds row 16i + l16 and 4
-    // consecutive columns of each subtile: one 8-byte access each when they
-    // are all in range and N % 4 == 0
+    // ---- epilogue: D = bf16(acc + C), through LDS.  The waves write the
+    // fp32 sums of CH of their subtile rows (WGM * CH * 16 rows of the tile)
+    // into stage 0, then every thread stores 8-column row segments of D (16
+    // bytes, with the matching 16 bytes of C added): whole lines of D leave
+    // the workgroup at once, rather than the 32-byte pieces one wave holds
+    constexpr int CH = epi_rows(SM, WGM, BN, STAGE);
+    constexpr int PITCH = BN + 4;                      // floats per staged row
+    constexpr int SEGS = BN / 8;                       // 16-byte segments per row
+    constexpr int ITEMS = WGM * CH * 16 * SEGS;
     const uint16_t *C = p.c;
     uint16_t *Dp = p.d;
-    const bool vec = (N % 4) == 0;
-    static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        const int row = (wm * SM + i) * 16 + l16;
-        if (row < M) {
+    float *stage = reinterpret_cast<float *>(stage0);
+    const bool vec = (N % 8) == 0;
+    static_for<SM / CH>([&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value;
+        lds_barrier();                                 // the stage is free: its last reads are done
+        static_for<CH>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int ii = decltype(ic)::value;
             static_for<SN>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
-                const int col = n0 + (wn * SN + j) * 16 + 4 * g4;
-                const int64_t o = (int64_t)row * N + col;
-                float v[4] = {acc[i][j].x, acc[i][j].y, acc[i][j].z, acc[i][j].w};
-                if (vec && col + 3 < N) {
-                    if (C) {
-                        const uint2 cw = *reinterpret_cast<const uint2 *>(C + o);
-                        v[0] += bf16_to_f32((uint16_t)(cw.x & 0xffff));
-                        v[1] += bf16_to_f32((uint16_t)(cw.x >> 16));
-                        v[2] += bf16_to_f32((uint16_t)(cw.y & 0xffff));
-                        v[3] += bf16_to_f32((uint16_t)(cw.y >> 16));
-                    }
-                    const uint32_t w0 = pack_bf16x2_rne(v[0], v[1]), w1 = pack_bf16x2_rne(v[2], v[3]);
-                    __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t *>(Dp + o));
-                    __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t *>(Dp + o) + 1);
-                } else {
+                // row 16i + l%16 and columns 16j + 4(l/16) .. +3 of the wave's subtiles
+                *reinterpret_cast<v4f *>(stage + ((wm * CH + ii) * 16 + l16) * PITCH + (wn * SN + j) * 16 + 4 * g4) =
+                    acc[c * CH + ii][j];
+            });
+        });
+        lds_barrier();
+        for (int item = tid; item < ITEMS; item += 64 * NW) {
+            const int sr = item / SEGS, sg = item - sr * SEGS;
+            const int row = (sr / (CH * 16)) * SM * 16 + (c * CH + (sr / 16) % CH) * 16 + sr % 16;
+            const int col = n0 + sg * 8;
+            if (row >= M || col >= N) continue;
+            const float *sp = stage + sr * PITCH + sg * 8;
+            const v4f lo = *reinterpret_cast<const v4f *>(sp);
+            const v4f hi = *reinterpret_cast<const v4f *>(sp + 4);
+            float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const int64_t o = (int64_t)row * N + col;
+            if (vec) {
+                if (C) {
+                    const v4i cw = *reinterpret_cast<const v4i *>(C + o);
+                    const int cv[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        if (col + e < N) {
-                            float out = v[e];
-                            if (C) out += bf16_to_f32(C[o + e]);
-                            Dp[o + e] = f32_to_bf16_rne(out);
-                        }
+                        v[2 * e] += bf16_to_f32((uint16_t)((uint32_t)cv[e] & 0xffff));
+                        v[2 * e + 1] += bf16_to_f32((uint16_t)((uint32_t)cv[e] >> 16));
                     }
                 }
-            });
+                const v4i w = v4i{(int)pack_bf16x2_rne(v[0], v[1]), (int)pack_bf16x2_rne(v[2], v[3]),
+                                  (int)pack_bf16x2_rne(v[4], v[5]), (int)pack_bf16x2_rne(v[6], v[7])};
+                __builtin_nontemporal_store(w, reinterpret_cast<v4i *>(Dp + o));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (col + e < N) {
+                        float out = v[e];
+                        if (C) out += bf16_to_f32(C[o + e]);
+                        Dp[o + e] = f32_to_bf16_rne(out);
+                    }
+                }
+            }
         }
     });
 }
