@@ -96,6 +96,34 @@ def test_masked_every_family(family):
     assert _family_of(cfg) == family, cfg
 
 
+@pytest.mark.parametrize("family", FAMILIES, indirect=True)
+def test_masked_padding_rows_are_inert(family):
+    """Rows at or past masked_m hold E4M3 NaN codes in A and NaN scales in
+    sfa: the valid rows still equal the oracle's (computed on the clean
+    inputs) and no padding row of D is written."""
+    counts = [0, 5, 64, 65, 130, 256]
+    G, M_cap, N, K = len(counts), 256, 392, 512
+    announce(f"family={family} masked with poisoned padding rows {counts}")
+    p = masked_problem(G, M_cap, N, K, counts, seed=31, with_c=True)
+    a, sfa = p["a"].copy(), p["sfa"].copy()
+    for g, mm in enumerate(counts):
+        a[g, mm:, :] = 0x7F                      # E4M3FN NaN
+        sfa[g, :, mm:] = np.nan
+    out = Guarded((G, M_cap, N))
+    dg.m_grouped_fp8_gemm_nt_masked(dev(a), dev(sfa), dev(p["b"]), dev(p["sfb"]), out.t,
+                                    dev(p["masked_m"]), expected_m=64, c=dev_bf16(p["c"]))
+    torch.cuda.synchronize()
+    cfg = dg.last_config()
+    assert out.guards_intact()
+    got = out.bits()
+    ref = oracle.m_grouped_masked(p["a"], p["sfa"], p["b"], p["sfb"], p["c"], p["masked_m"])
+    for g, mm in enumerate(counts):
+        if mm:
+            check_close(got[g, :mm], ref[g, :mm], f"{family} poisoned masked group {g} ({cfg})")
+        assert np.all(got[g, mm:] == SENTINEL), f"{family} group {g}: padding rows written"
+    assert _family_of(cfg) == family, cfg
+
+
 @pytest.mark.parametrize("family", ["pipe", "persist", "tiled"], indirect=True)
 def test_contiguous_every_family(family):
     counts = [130, 1, 0, 257, 128, 60]
@@ -112,6 +140,32 @@ def test_contiguous_every_family(family):
     ref = oracle.m_grouped_contiguous(p["a"], p["sfa"], p["b"], p["sfb"], p["c"], p["m_indices"])
     valid = p["m_indices"] >= 0
     check_close(got[valid], ref[valid], f"{family} contiguous valid rows ({cfg})")
+    assert np.all(got[~valid] == SENTINEL)
+    assert _family_of(cfg) == family, cfg
+
+
+@pytest.mark.parametrize("family", ["pipe", "persist", "tiled"], indirect=True)
+def test_contiguous_padding_rows_are_inert(family):
+    """Padding rows (m_indices = -1) hold E4M3 NaN codes in A and NaN scales
+    in sfa: the valid rows still equal the oracle's (computed on the clean
+    inputs) and no padding row of D is written."""
+    counts = [130, 1, 0, 257, 128, 60]
+    N, K = 520, 640
+    announce(f"family={family} contiguous with poisoned padding rows {counts}")
+    p = contiguous_problem(counts, N, K, seed=37, with_c=True)
+    valid = p["m_indices"] >= 0
+    a, sfa = p["a"].copy(), p["sfa"].copy()
+    a[~valid, :] = 0x7F                          # E4M3FN NaN
+    sfa[:, :p["M_total"]][:, ~valid] = np.nan
+    out = Guarded((p["M_total"], N))
+    dg.m_grouped_fp8_gemm_nt_contiguous(dev(a), dev(sfa), dev(p["b"]), dev(p["sfb"]), out.t,
+                                        dev(p["m_indices"]), c=dev_bf16(p["c"]))
+    torch.cuda.synchronize()
+    cfg = dg.last_config()
+    assert out.guards_intact()
+    got = out.bits()
+    ref = oracle.m_grouped_contiguous(p["a"], p["sfa"], p["b"], p["sfb"], p["c"], p["m_indices"])
+    check_close(got[valid], ref[valid], f"{family} poisoned contiguous valid rows ({cfg})")
     assert np.all(got[~valid] == SENTINEL)
     assert _family_of(cfg) == family, cfg
 
