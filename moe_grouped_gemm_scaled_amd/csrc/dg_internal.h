@@ -110,8 +110,9 @@ inline bool take_splitk_scratch(const GemmProblem &p, size_t partial_bytes, size
 bool skinny_eligible(const GemmProblem &p);
 hipError_t launch_skinny(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
 
-// Streaming family for decode shapes (dense, M <= 128): B loaded straight
-// into a per-wave register ring, A through an LDS ring, optional split-K.
+// Streaming family for decode shapes (dense, M <= 128): all rows of A and a
+// column tile of B per workgroup, one K block per LDS stage filled by DMA,
+// optional split-K.
 bool stream_eligible(const GemmProblem &p);
 hipError_t launch_stream(const GemmProblem &p, int num_cus, hipStream_t stream, std::string &config);
 
