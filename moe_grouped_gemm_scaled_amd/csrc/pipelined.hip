@@ -637,28 +637,44 @@ pipe_kernel(PipeParams p) {
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     lds_barrier();
 
-    // ---- K-grouped epilogue: fp32 D = C + acc straight from the registers
-    // (lane l holds row 16i + l%16 and columns 16j + 4(l/16) .. +3 of its
-    // wave's tile: one 16-byte access each; M and N are multiples of 16)
+    // ---- K-grouped epilogue: fp32 D = C + acc.  Each wave stages EPI_ROWS
+    // rows of its tile at a time in its LDS area and reads them back as 4
+    // consecutive columns per lane, consecutive lanes along the row, so that
+    // one store instruction writes whole lines of D (from the registers, a
+    // lane holds 4 columns of 16 rows: half a line per row per instruction).
+    // M and N are multiples of 16.
     if constexpr (KG) {
         float *D32 = p.d32 + (int64_t)grp * rows_a * N;
         const float *C32 = p.c32 ? p.c32 + (int64_t)grp * rows_a * N : nullptr;
-        static_for<SM>([&](auto ic) __attribute__((always_inline)) {
-            constexpr int i = decltype(ic)::value;
-            const int row = m0 + wm * TM + 16 * i + l16;
-            v4f cv[SN];
-            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                constexpr int j = decltype(jc)::value;
-                const int col = n0 + wn * TN + 16 * j + 4 * g4;
-                cv[j] = v4f{0.f, 0.f, 0.f, 0.f};
-                if (C32 && row < rows_a && col < N)
-                    cv[j] = *reinterpret_cast<const v4f *>(C32 + (int64_t)row * N + col);
+        float *stg32 = reinterpret_cast<float *>(wave < NW / 2 ? stage0 : stage1) +
+                       (wave % (NW / 2)) * (EPI_ROWS * EPI_PITCH);
+        constexpr int SEG4 = TN / 4;                 // 16-byte segments per row
+        constexpr int NQ4 = EPI_ROWS * SEG4 / 64;    // items per lane per chunk
+        static_assert((EPI_ROWS * SEG4) % 64 == 0, "K-grouped epilogue items");
+        const int row0 = m0 + wm * TM, col0 = n0 + wn * TN;
+        static_for<TM / EPI_ROWS>([&](auto cc) __attribute__((always_inline)) {
+            constexpr int c = decltype(cc)::value;
+            static_for<EPI_ROWS / 16>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int ii = decltype(ic)::value;
+                static_for<SN>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    // row 16i + l%16, columns 16j + 4(l/16) .. +3
+                    *reinterpret_cast<v4f *>(stg32 + (ii * 16 + l16) * EPI_PITCH + j * 16 + 4 * g4) =
+                        acc[c * (EPI_ROWS / 16) + ii][j];
+                });
             });
-            static_for<SN>([&](auto jc) __attribute__((always_inline)) {
-                constexpr int j = decltype(jc)::value;
-                const int col = n0 + wn * TN + 16 * j + 4 * g4;
-                if (row < rows_a && col < N)
-                    __builtin_nontemporal_store(acc[i][j] + cv[j], reinterpret_cast<v4f *>(D32 + (int64_t)row * N + col));
+            static_for<NQ4>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                const int item = q * 64 + lane;
+                const int rl = item / SEG4, sg = item % SEG4;
+                const int row = row0 + c * EPI_ROWS + rl;
+                const int col = col0 + 4 * sg;
+                if (row < rows_a && col < N) {
+                    v4f v = *reinterpret_cast<const v4f *>(stg32 + rl * EPI_PITCH + 4 * sg);
+                    const int64_t o = (int64_t)row * N + col;
+                    if (C32) v += *reinterpret_cast<const v4f *>(C32 + o);
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(D32 + o));
+                }
             });
         });
         return;
